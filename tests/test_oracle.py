@@ -1,0 +1,410 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+* storage decoders: every bf16 and e4m3fn code against torch's casts;
+* attention value: a library routine (torch SDPA in float64 with grouped
+  query heads) on contiguous K/V that the test scatters into a pool itself;
+* brute force: pure-Python loops over the tiny case;
+* invariants: physical-block permutation, prefix aliasing, weights sum to 1;
+* closed forms: one token, zero query, constant values, one dominant key;
+* planted mistakes: a wrong head mapping, a wrong V layout, a dropped scale
+  or an off-by-one length in the oracle must break the SDPA pin.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import decode as odecode
+from oracle import numerics
+from paged_kv_cache_451_amd.workloads import CONFIG_BY_NAME, build_case
+
+from conftest import appended_pools, oracle_args, raw
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BS = 16
+
+
+# ---------------------------------------------------------------------------
+# storage decoders
+# ---------------------------------------------------------------------------
+def test_bf16_decoder_all_codes():
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = numerics.bf16_bits_to_f64(codes)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16) \
+        .to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_e4m3fn_decoder_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = numerics.e4m3fn_bits_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn) \
+        .to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert set(np.flatnonzero(nan).tolist()) == {0x7F, 0xFF}
+    assert np.nanmax(ours) == 448.0
+
+
+# ---------------------------------------------------------------------------
+# dense-equality pin (library routine)
+# ---------------------------------------------------------------------------
+def _dense_case(seed, *, lens, hq, hkv, d, dtype, nb=None, k_scale=1.0,
+                v_scale=1.0):
+    """Contiguous per-sequence K/V, scattered into a shuffled pool token by
+    token straight from the layout definition (K [NB,Hkv,16,D] and V
+    [NB,Hkv,D,16]).  Returns oracle arguments and the contiguous tensors."""
+    g = torch.Generator().manual_seed(seed)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16,
+           "fp8_e4m3fn": torch.float8_e4m3fn}[dtype]
+    need = sum(-(-n // BS) for n in lens)
+    nb = nb or need + 5
+    perm = torch.randperm(nb, generator=g).tolist()
+    kpool = torch.zeros(nb, hkv, BS, d, dtype=torch.float32).to(tdt)
+    vpool = torch.zeros(nb, hkv, d, BS, dtype=torch.float32).to(tdt)
+    width = max(-(-n // BS) for n in lens)
+    tables = np.full((len(lens), width), -1, dtype=np.int32)
+    kcs, vcs, nxt = [], [], 0
+    for b, n in enumerate(lens):
+        kc = torch.randn(n, hkv, d, generator=g).to(tdt)
+        vc = torch.randn(n, hkv, d, generator=g).to(tdt)
+        for j in range(-(-n // BS)):
+            tables[b, j] = perm[nxt]
+            nxt += 1
+        for t in range(n):
+            phys, off = int(tables[b, t // BS]), t % BS
+            kpool[phys, :, off, :] = kc[t]
+            vpool[phys, :, :, off] = vc[t]
+        kcs.append(kc.to(torch.float64) * k_scale)
+        vcs.append(vc.to(torch.float64) * v_scale)
+    q = torch.randn(len(lens), hq, d, generator=g)
+    qdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = q.to(qdt)
+    qraw, qname = raw(q)
+    kraw, kname = raw(kpool)
+    vraw, _ = raw(vpool)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    args = dict(q=qraw, k_raw=kraw, v_raw=vraw, block_tables=tables,
+                seq_lens=np.array(lens, dtype=np.int32), scale=scale,
+                q_dtype=qname, kv_dtype=kname, k_scale=k_scale,
+                v_scale=v_scale)
+    return args, q.to(torch.float64), kcs, vcs
+
+
+def _sdpa(q64, kcs, vcs, scale):
+    outs = []
+    for b, (kc, vc) in enumerate(zip(kcs, vcs)):
+        qq = q64[b][None, :, None, :]                # [1, Hq, 1, D]
+        kk = kc.permute(1, 0, 2)[None]               # [1, Hkv, L, D]
+        vv = vc.permute(1, 0, 2)[None]
+        o = F.scaled_dot_product_attention(
+            qq, kk, vv, scale=float(np.float64(np.float32(scale))),
+            enable_gqa=True)
+        outs.append(o[0, :, 0, :].numpy())
+    return np.stack(outs)
+
+
+DENSE_CASES = [
+    dict(lens=[1, 17, 40, 33], hq=2, hkv=2, d=64, dtype="f32"),
+    dict(lens=[16, 100, 257], hq=8, hkv=2, d=128, dtype="bf16"),
+    dict(lens=[300, 5, 64], hq=12, hkv=3, d=64, dtype="bf16"),
+    dict(lens=[90, 31], hq=4, hkv=1, d=128, dtype="fp8_e4m3fn",
+         k_scale=0.0123, v_scale=0.0071),
+]
+
+
+@pytest.mark.parametrize("spec", DENSE_CASES)
+def test_paged_equals_dense_sdpa(spec):
+    args, q64, kcs, vcs = _dense_case(7, **spec)
+    ours = oracle.paged_decode(**args)
+    ref = _sdpa(q64, kcs, vcs, args["scale"])
+    assert np.abs(ours - ref).max() <= 1e-12
+
+
+# planted mistakes: each mutated oracle must fail the same pin -------------
+def _pin_fails(args, q64, kcs, vcs, **override):
+    ours = oracle.paged_decode(**{**args, **override})
+    ref = _sdpa(q64, kcs, vcs, args["scale"])
+    return not (np.abs(ours - ref).max() <= 1e-12)
+
+
+def test_planted_wrong_head_mapping_is_caught(monkeypatch):
+    args, q64, kcs, vcs = _dense_case(7, **DENSE_CASES[1])
+    monkeypatch.setattr(odecode, "_kv_head_of",
+                        lambda h, hq, hkv: h % hkv)
+    assert _pin_fails(args, q64, kcs, vcs)
+
+
+def test_planted_wrong_v_layout_is_caught(monkeypatch):
+    args, q64, kcs, vcs = _dense_case(7, **DENSE_CASES[1])
+    real = odecode.gather_sequence
+
+    def v_as_token_major(k_raw, v_raw, table_row, seq_len, kv_dtype,
+                         k_scale=1.0, v_scale=1.0):
+        k, _ = real(k_raw, v_raw, table_row, seq_len, kv_dtype, k_scale,
+                    v_scale)
+        # reads the V tile as if it were [16, D] like K (wrong layout)
+        _, v = real(k_raw, v_raw.reshape(k_raw.shape), table_row, seq_len,
+                    kv_dtype, k_scale, v_scale)
+        return k, v.reshape(k.shape)
+
+    monkeypatch.setattr(odecode, "gather_sequence", v_as_token_major)
+    assert _pin_fails(args, q64, kcs, vcs)
+
+
+def test_planted_dropped_scale_is_caught():
+    args, q64, kcs, vcs = _dense_case(7, **DENSE_CASES[0])
+    assert _pin_fails(args, q64, kcs, vcs, scale=1.0)
+
+
+def test_planted_off_by_one_length_is_caught():
+    args, q64, kcs, vcs = _dense_case(7, **DENSE_CASES[0])
+    assert _pin_fails(args, q64, kcs, vcs, seq_lens=args["seq_lens"] - 1)
+
+
+# ---------------------------------------------------------------------------
+# brute force on the tiny case
+# ---------------------------------------------------------------------------
+def test_bruteforce_tiny_case():
+    case = build_case(CONFIG_BY_NAME["tiny_fp32"], seed=0)
+    kp, vp = appended_pools(case)
+    ours = oracle.paged_decode(**oracle_args(case), **{})  # pre-append: NaN
+    assert np.isnan(ours).any()  # the new token's slot is poisoned before
+    args = oracle_args(case)
+    args.update(k_raw=kp, v_raw=vp)
+    ours = oracle.paged_decode(**args)
+
+    q = case.q.tolist()
+    K, V = kp.tolist(), vp.tolist()
+    tab = case.block_tables.tolist()
+    hq, hkv = case.config.num_q_heads, case.config.num_kv_heads
+    d = case.config.head_size
+    sc = float(np.float32(case.scale))
+    for b, n in enumerate(case.seq_lens.tolist()):
+        for h in range(hq):
+            g = h // (hq // hkv)
+            s = []
+            for t in range(n):
+                phys, off = tab[b][t // BS], t % BS
+                s.append(sc * sum(q[b][h][i] * K[phys][g][off][i]
+                                  for i in range(d)))
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = sum(e)
+            for i in range(d):
+                acc = 0.0
+                for t in range(n):
+                    phys, off = tab[b][t // BS], t % BS
+                    acc += e[t] / z * V[phys][g][i][off]
+                assert abs(acc - ours[b, h, i]) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+def _small(name, **kw):
+    return build_case(CONFIG_BY_NAME[name].replace(**kw), seed=3)
+
+
+def test_physical_block_permutation_is_bitwise_invariant():
+    case = _small("llama3_8b_bf16", num_seqs=5, lo=20, hi=300)
+    kp, vp = appended_pools(case)
+    args = oracle_args(case)
+    args.update(k_raw=kp, v_raw=vp)
+    ref = oracle.paged_decode(**args)
+    rng = np.random.default_rng(11)
+    pi = rng.permutation(kp.shape[0])
+    kq, vq = np.empty_like(kp), np.empty_like(vp)
+    kq[pi], vq[pi] = kp, vp
+    tab = args["block_tables"]
+    tab2 = np.where(tab >= 0, pi[np.maximum(tab, 0)], -1).astype(np.int32)
+    out = oracle.paged_decode(**{**args, "k_raw": kq, "v_raw": vq,
+                                 "block_tables": tab2})
+    assert np.array_equal(out, ref)
+
+
+def test_prefix_aliasing_is_bitwise_invariant():
+    case = _small("prefix_shared_bf16", num_seqs=6, prefix_len=64, lo=5,
+                  hi=40)
+    kp, vp = appended_pools(case)
+    args = oracle_args(case)
+    args.update(k_raw=kp, v_raw=vp)
+    tab = args["block_tables"].copy()
+    npre = 64 // BS
+    shared = tab[0, :npre].copy()
+    assert all(np.array_equal(tab[i, :npre], shared) for i in range(6))
+    assert all(case.ref_cnt[p] == 6 for p in shared)
+    ref = oracle.paged_decode(**args)
+    # give every later sequence private copies of the prefix blocks
+    kparts, vparts = [kp], [vp]
+    nxt = kp.shape[0]
+    for i in range(1, 6):
+        kparts.append(kp[shared])
+        vparts.append(vp[shared])
+        tab[i, :npre] = np.arange(nxt, nxt + npre)
+        nxt += npre
+    out = oracle.paged_decode(**{**args, "k_raw": np.concatenate(kparts),
+                                 "v_raw": np.concatenate(vparts),
+                                 "block_tables": tab})
+    assert np.array_equal(out, ref)
+
+
+def test_softmax_weights_sum_to_one():
+    case = _small("skewed_bf16", num_seqs=3, hi=700)
+    kp, vp = appended_pools(case)
+    args = oracle_args(case)
+    args.update(k_raw=kp, v_raw=vp)
+    for s in range(3):
+        w = oracle.attention_weights(**args, seq=s)
+        assert w.shape[1] == int(case.seq_lens[s])
+        assert np.abs(w.sum(axis=1) - 1.0).max() <= 1e-12
+        assert (w >= 0).all()
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+def _one_seq(n, *, q=None, v_fill=None, hq=4, hkv=2, d=64, seed=5):
+    args, q64, kcs, vcs = _dense_case(seed, lens=[n], hq=hq, hkv=hkv, d=d,
+                                      dtype="f32")
+    if q is not None:
+        args["q"] = np.full_like(args["q"], q)
+    if v_fill is not None:
+        args["v_raw"] = np.full_like(args["v_raw"], v_fill)
+    return args
+
+
+def test_single_token_returns_its_value_row():
+    args = _one_seq(1)
+    out = oracle.paged_decode(**args)
+    phys = int(args["block_tables"][0, 0])
+    for h in range(4):
+        assert np.array_equal(out[0, h], args["v_raw"][phys, h // 2, :, 0]
+                              .astype(np.float64))
+
+
+def test_zero_query_gives_mean_of_values():
+    args = _one_seq(37, q=0.0)
+    out = oracle.paged_decode(**args)
+    tab = args["block_tables"][0]
+    rows = np.stack([args["v_raw"][tab[t // BS], :, :, t % BS]
+                     for t in range(37)]).astype(np.float64)
+    for h in range(4):
+        assert np.abs(out[0, h] - rows[:, h // 2, :].mean(0)).max() <= 1e-12
+
+
+def test_constant_values_give_that_constant():
+    args = _one_seq(50, v_fill=0.375)
+    out = oracle.paged_decode(**args)
+    assert np.abs(out - 0.375).max() <= 1e-12
+
+
+def test_dominant_key_selects_its_row():
+    args = _one_seq(45, q=1.0)
+    tab = args["block_tables"][0]
+    hot = 29
+    args["k_raw"][tab[hot // BS], :, hot % BS, :] = 100.0
+    out = oracle.paged_decode(**args)
+    row = args["v_raw"][tab[hot // BS], :, :, hot % BS].astype(np.float64)
+    for h in range(4):
+        assert np.abs(out[0, h] - row[h // 2]).max() <= 1e-9
+
+
+def test_zero_length_sequence_gives_zero_row():
+    args = _one_seq(20)
+    args["seq_lens"] = np.array([0], dtype=np.int32)
+    out = oracle.paged_decode(**args)
+    assert np.array_equal(out, np.zeros_like(out))
+
+
+# ---------------------------------------------------------------------------
+# KV append
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_fp32", "prefix_shared_bf16",
+                                  "fp8_long"])
+def test_append_lands_where_decode_reads_it(name):
+    cfg = CONFIG_BY_NAME[name]
+    if name != "tiny_fp32":
+        cfg = cfg.replace(num_seqs=6, lo=40, hi=200,
+                          prefix_len=min(cfg.prefix_len, 64))
+    case = build_case(cfg, seed=1)
+    k0, kdt = raw(case.k_pool)
+    v0, _ = raw(case.v_pool)
+    kn, _ = raw(case.k_new)
+    vn, _ = raw(case.v_new)
+    k1, v1 = oracle.kv_append(k0, v0, kn, vn, case.slot_mapping.numpy())
+    # the new token is the last token each sequence's table walk reaches
+    for i, n in enumerate(case.seq_lens.tolist()):
+        kc, vc = odecode.gather_sequence(k1, v1, case.block_tables[i].numpy(),
+                                         n, kdt)
+        assert np.array_equal(kc[n - 1], numerics.widen(kn[i], kdt))
+        assert np.array_equal(vc[n - 1], numerics.widen(vn[i], kdt))
+    # nothing else changes: exactly one K row and one V column per token
+    dk = (k0.view(np.uint8) != k1.view(np.uint8)).reshape(k0.shape[0], -1)
+    changed_blocks = set(np.flatnonzero(dk.any(1)).tolist())
+    assert changed_blocks == {s // BS for s in case.slot_mapping.tolist()}
+    item = k0.dtype.itemsize
+    per_tok = case.config.num_kv_heads * case.config.head_size * item
+    assert int(dk.sum()) <= len(case.slot_mapping) * per_tok
+    # the pool before the append held NaN exactly where the new tokens go
+    assert np.isnan(numerics.widen(k0, kdt)).any()
+
+
+def test_append_skips_negative_and_out_of_range_slots():
+    k = np.zeros((3, 2, BS, 8), dtype=np.uint16)
+    v = np.zeros((3, 2, 8, BS), dtype=np.uint16)
+    kn = np.ones((3, 2, 8), dtype=np.uint16)
+    k1, v1 = oracle.kv_append(k, v, kn, kn, np.array([-1, 3 * BS, 5]))
+    assert int((k1 != 0).sum()) == 16 and int((v1 != 0).sum()) == 16
+    assert (k1[0, :, 5, :] == 1).all() and (v1[0, :, :, 5] == 1).all()
+
+
+# ---------------------------------------------------------------------------
+# block / byte arithmetic and the capacity example
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_bf16",
+                                  "fp8_long"])
+def test_block_bytes_formula(name):
+    cfg = CONFIG_BY_NAME[name]
+    if name != "tiny_fp32":
+        cfg = cfg.replace(num_seqs=3, lo=16, hi=100)
+    case = build_case(cfg, seed=0)
+    s = case.k_pool.element_size()
+    per_block = oracle.capacity.block_bytes(16, cfg.num_kv_heads,
+                                            cfg.head_size, s)
+    total = case.k_pool.numel() * s + case.v_pool.numel() * s
+    assert total == case.num_blocks * per_block
+    # fp8 storage halves the bytes of a 16-bit block
+    assert oracle.capacity.block_bytes(16, 8, 128, 1) * 2 == \
+        oracle.capacity.block_bytes(16, 8, 128, 2) == 65536
+    # one request's cache: 2 x layers x heads x head dim x tokens elements
+    n = int(case.seq_lens[0])
+    kc, vc = odecode.gather_sequence(raw(case.k_pool)[0], raw(case.v_pool)[0],
+                                     case.block_tables[0].numpy(), n,
+                                     raw(case.k_pool)[1])
+    assert kc.size + vc.size == oracle.capacity.request_kv_elements(
+        1, cfg.num_kv_heads, cfg.head_size, n)
+
+
+def test_capacity_example_matches_printed_numbers():
+    ex = json.load(open(os.path.join(GOLDEN, "capacity_example.json")))
+    cap = oracle.capacity
+    contig = cap.contiguous_capacity(ex["pool"], ex["block"], ex["max_len"])
+    fcfs, used = cap.paged_capacity_fcfs(ex["pool"], ex["block"], ex["lens"])
+    skip, _ = cap.paged_capacity_skip(ex["pool"], ex["block"], ex["lens"])
+    assert (contig, fcfs) == (ex["printed_contiguous"], ex["printed_paged"])
+    assert skip == 14  # the loop exactly as printed (no stop at a miss)
+    assert used == 118
+    # utilisation: contiguous ~20-40 % (the pages' range), paged near 100 %
+    contig_util = sum(ex["lens"][:contig]) / (contig * ex["max_len"])
+    paged_util = sum(ex["lens"][:fcfs]) / (used * ex["block"])
+    assert round(contig_util, 3) == 0.260 and 0.20 <= contig_util <= 0.40
+    assert round(paged_util, 3) == 0.958
