@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of one paged decode step on one MI355X.
+
+A step is the whole hot path over one batch: ``pa_kv_append`` of each
+sequence's new token, then ``pa_decode`` (main pass + merge pass) over every
+sequence's paged context.  Inputs are synthetic and seeded (see
+``paged_kv_cache_451_amd/workloads.py``); they are resident in HBM before
+timing starts.  Successive steps rotate over several copies of the K/V pool,
+like successive layers of a model, so no step finds the previous step's
+blocks in L2 or the Infinity Cache.
+
+Prints one JSON line.  ``value`` is the step's algorithmic bytes (each cached
+token's K and V read once per KV head, q in, out out, table entries, the
+append's read+write) divided by the wall time per step.  ``roofline``
+reports the main decode kernel alone, timed with HIP events recorded on the
+launch stream around it, against the 8 TB/s HBM peak.  ``cpu_baseline`` times
+the float64 CPU oracle on a sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+METRIC = ("paged decode attention: achieved HBM GB/s (% of MI355X peak) + "
+          "seqs·tokens/s")
+ROOT = os.path.dirname(os.path.abspath(__file__))
+MAIN_KERNEL_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "pa_device.h")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default="llama3_8b_bf16")
+    p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--num-waves", type=int, default=0)
+    p.add_argument("--rotate", type=int, default=0,
+                   help="pool copies to rotate over (0: enough for >= 2 GiB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in MAIN_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_451_amd", "csrc", name),
+                  "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_name: str):
+    """HBM bytes per main-kernel launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"decode_{config_name}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float):
+    """Float64 oracle over whole sequences until ~budget_s of CPU time."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from oracle.adapters import appended_pools, oracle_args
+    from paged_kv_cache_451_amd.workloads import DTYPE_BYTES
+
+    cfg = case.config
+    kp, vp = appended_pools(case)
+    args = oracle_args(case)
+    args.update(k_raw=kp, v_raw=vp)
+    lens = case.seq_lens.numpy()
+    done, t_total, tokens = [], 0.0, 0
+    for i in range(len(lens)):
+        t0 = time.perf_counter()
+        oracle.paged_decode(**args, seqs=[i])
+        t_total += time.perf_counter() - t0
+        done.append(i)
+        tokens += int(lens[i])
+        if t_total >= budget_s:
+            break
+    s_kv = DTYPE_BYTES[cfg.kv_dtype]
+    kv_bytes = tokens * cfg.num_kv_heads * cfg.head_size * 2 * s_kv
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": round(kv_bytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle over the first {len(done)} of "
+                   f"{len(lens)} sequences ({tokens} context tokens, "
+                   f"{t_total:.1f} s); KV bytes read per second"),
+        "context_tokens_per_s": round(tokens / t_total, 1),
+        "decode_tokens_per_s": round(len(done) / t_total, 3),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); "
+              "the decode path has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_451_amd import _lib
+    from paged_kv_cache_451_amd.workloads import (CONFIG_BY_NAME, CONFIGS,
+                                                  algorithmic_bytes,
+                                                  build_case)
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    _lib.load()
+    cfg = CONFIG_BY_NAME[a.config]
+    seed = a.seed if a.seed is not None else \
+        [c.name for c in CONFIGS].index(cfg.name)
+    t0 = time.time()
+    case = build_case(cfg, seed)
+    print(f"[bench] built {cfg.name} (seed {seed}) in {time.time()-t0:.1f}s",
+          file=sys.stderr, flush=True)
+    nbytes = algorithmic_bytes(case)
+
+    dev = torch.device("cuda:0")
+    q = case.q.to(dev)
+    tables = case.block_tables.to(dev)
+    lens = case.seq_lens.to(dev)
+    slots = case.slot_mapping.to(dev)
+    k_new = case.k_new.to(dev)
+    v_new = case.v_new.to(dev)
+    pool_bytes = (case.k_pool.numel() * case.k_pool.element_size()) * 2
+    nrot = a.rotate or max(2, math.ceil((2 << 30) / pool_bytes))
+    kps = [case.k_pool.to(dev)]
+    vps = [case.v_pool.to(dev)]
+    for _ in range(nrot - 1):
+        kps.append(kps[0].clone())
+        vps.append(vps[0].clone())
+    out = torch.empty_like(q)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+          for _ in range(a.steps)]
+    stream = torch.cuda.current_stream()
+    for pair in ev:  # create the underlying HIP events
+        for e in pair:
+            e.record(stream)
+    torch.cuda.synchronize()
+
+    def desc_for(events=None):
+        return _lib.decode_desc(
+            q, kps[0], tables, max_seq_len=case.max_seq_len,
+            k_scale=case.k_scale, v_scale=case.v_scale,
+            total_blocks_hint=case.total_blocks, num_waves=a.num_waves,
+            events=events)
+
+    base_desc = desc_for()
+    ws = _lib.alloc_workspace(base_desc, dev)
+    descs = [desc_for((e0.cuda_event, e1.cuda_event)) for e0, e1 in ev]
+
+    def step(i, desc):
+        kp, vp = kps[i % nrot], vps[i % nrot]
+        _lib.pa_kv_append(k_new, v_new, slots, kp, vp)
+        _lib.pa_decode(q, kp, vp, tables, lens, case.scale, out,
+                       max_seq_len=case.max_seq_len, workspace=ws, desc=desc)
+
+    for i in range(a.warmup):
+        step(i, base_desc)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({a.warmup} steps, {nrot} pool copies)",
+          file=sys.stderr, flush=True)
+
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(a.warmup + i, descs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / a.steps
+    kern_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    kern_ms.sort()
+    k_avg = sum(kern_ms) / len(kern_ms)
+    k_med = kern_ms[len(kern_ms) // 2]
+
+    value = nbytes["step"] / (ms_step * 1e-3) / 1e9
+    achieved = nbytes["decode"] / (k_avg * 1e-3) / 1e9
+    traffic = measured_traffic(cfg.name)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.q_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "description": cfg.description,
+            "batch": cfg.num_seqs, "num_q_heads": cfg.num_q_heads,
+            "num_kv_heads": cfg.num_kv_heads, "head_size": cfg.head_size,
+            "block_size": 16, "kv_dtype": cfg.kv_dtype,
+            "context_tokens": nbytes["context_tokens"],
+            "max_seq_len": case.max_seq_len, "num_blocks": case.num_blocks,
+            "seed": seed, "pool_copies_rotated": nrot,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(cfg.num_seqs / (ms_step * 1e-3), 1),
+        "context_tokens_per_s": round(
+            nbytes["context_tokens"] / (ms_step * 1e-3), 1),
+        "bytes_per_step": nbytes["step"],
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_mfma_kernel" if cfg.kv_dtype != "f32"
+            else "decode_valu_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": nbytes["decode"],
+            "kernel_ms_avg": round(k_avg, 5),
+            "kernel_ms_median": round(k_med, 5),
+            "kernel_ms_p10": round(kern_ms[len(kern_ms) // 10], 5),
+            "kernel_ms_p90": round(kern_ms[(9 * len(kern_ms)) // 10], 5),
+        },
+        "cpu_baseline": None,
+    }
+    if cfg.lens == "prefix":
+        res["roofline"]["achieved_unique"] = round(
+            nbytes["decode_unique"] / (k_avg * 1e-3) / 1e9, 2)
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(case, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * pa.h - C ABI of the gfx950 paged decode-attention library (libpa.so).
+ *
+ * Two operations, both from the paged KV-cache design:
+ *
+ *   pa_kv_append  writes each new token's K and V into the pool slot the
+ *                 block manager reserved for it.  The block manager takes a
+ *                 fresh block only when the sequence's last block is full and
+ *                 then writes the token into that last block ("49 vLLM /
+ *                 PagedAttention", listing "Таблица блоков (идея пейджинга)";
+ *                 "PagedAttention：KV cache 即虚拟内存（block manager & 碎片）",
+ *                 section "深入原理", lifecycle bullet).
+ *
+ *   pa_decode     single-token decode attention over K/V that live in
+ *                 fixed 16-token blocks scattered through a shared pool, each
+ *                 sequence's block table mapping logical block t/16 to a
+ *                 physical block ("49 vLLM / PagedAttention", section "Идея и
+ *                 механизм"; "PagedAttention：KV cache 即虚拟内存", section
+ *                 "直接答案").  The result equals dense attention over the
+ *                 contiguous context (same page, sections "直接答案" and
+ *                 "面试官追问"):
+ *                     out[b,h,:] = sum_t softmax_t(scale * <q[b,h,:], K_t>) V_t
+ *                 over t < seq_lens[b], with query head h reading KV head
+ *                 h / (num_q_heads / num_kv_heads).
+ *
+ * Storage layouts (row-major, element counts):
+ *   q, out        [num_seqs][num_q_heads][head_size]
+ *   k_pool        [num_blocks][num_kv_heads][16][head_size]   (token rows)
+ *   v_pool        [num_blocks][num_kv_heads][head_size][16]   (tokens inner)
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens      int32 [num_seqs]
+ *   k_new, v_new  [num_tokens][num_kv_heads][head_size]
+ *   slot_mapping  int32 [num_tokens]; slot = physical_block * 16 + offset
+ * The byte count of one block is 2 * 16 * num_kv_heads * head_size * the
+ * element size ("vLLM innenfra", KV-cache-manager paragraph); the order of
+ * the axes inside a block is this library's choice: each (block, KV head)
+ * K tile and V tile is one contiguous 16*head_size run, and V is stored with
+ * the 16 tokens innermost so that the matrix-core contraction over tokens
+ * reads contiguous bytes.
+ *
+ * Ownership: every array argument is device memory owned by the caller; the
+ * library keeps no pointer after a call returns and allocates nothing.
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ * stream) and never synchronise the host.
+ *
+ * Errors: functions return PA_OK (0) or a negative pa_status from host-side
+ * checks (null pointers, unsupported shapes or dtypes, misaligned pointers,
+ * workspace too small) or from the launch itself.  Nothing is launched when a
+ * check fails.  Data-dependent contract violations are not reported but are
+ * contained: a slot outside [0, num_blocks*16) is skipped, a block-table
+ * entry outside [0, num_blocks) contributes nothing, a sequence length is
+ * clamped to [0, max_blocks_per_seq*16]; no access ever leaves the buffers.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_F32 = 0,         /* IEEE binary32 */
+  PA_BF16 = 1,        /* bfloat16 */
+  PA_FP8_E4M3FN = 2   /* OCP fp8 e4m3fn (bias 7, max 448, no inf) */
+} pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,         /* a required pointer is NULL */
+  PA_ERR_DTYPE = -2,        /* unsupported dtype combination */
+  PA_ERR_SHAPE = -3,        /* unsupported or inconsistent size */
+  PA_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned */
+  PA_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
+  PA_ERR_LAUNCH = -6,       /* the HIP runtime rejected a launch */
+  PA_ERR_DEVICE = -7        /* no usable HIP device */
+} pa_status;
+
+/*
+ * Shapes and options of one decode call.
+ *   num_seqs            B >= 0 (at most 65536)
+ *   num_q_heads         Hq, a multiple of num_kv_heads
+ *   num_kv_heads        Hkv >= 1
+ *   head_size           D in {64, 128, 256}
+ *   block_size          must be 16
+ *   num_blocks          NB >= 1, NB*16 <= INT32_MAX
+ *   max_blocks_per_seq  row length of block_tables (>= 1)
+ *   max_seq_len         upper bound of seq_lens (scheduling hint; >= 0)
+ *   q_dtype / kv_dtype  (F32, F32) or (BF16, BF16) or (BF16, FP8_E4M3FN);
+ *                       out has q_dtype.  G = Hq/Hkv must be <= 8 for F32 and
+ *                       <= 16 otherwise.
+ *   k_scale / v_scale   per-tensor dequantisation scales of an FP8 pool
+ *                       (stored value * scale = real value); ignored (use 1)
+ *                       for F32/BF16 pools.
+ *   total_blocks_hint   sum over b of ceil(seq_lens[b]/16) if the caller
+ *                       knows it, else 0; only balances the work split.
+ *   num_waves           0 = automatic; else the number of 64-lane
+ *                       workgroups of the main kernel (rounded to a multiple
+ *                       of num_kv_heads).
+ *   profile_events      NULL, or two hipEvent_t the call records on `stream`
+ *                       immediately before and after the main kernel.
+ */
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_size;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t max_seq_len;
+  pa_dtype q_dtype;
+  pa_dtype kv_dtype;
+  float k_scale;
+  float v_scale;
+  int64_t total_blocks_hint;
+  int32_t num_waves;
+  int32_t reserved;
+  void* profile_events[2];
+} pa_decode_desc;
+
+/*
+ * Bytes of device workspace pa_decode needs for `desc` on the current
+ * device (0 on an invalid descriptor).  The workspace holds the per-sequence
+ * block prefix sums and the split-context partial results; its contents
+ * need no initialisation and are scratch between calls.
+ */
+size_t pa_decode_workspace_size(const pa_decode_desc* desc);
+
+/*
+ * Decode attention (see the top of this file).
+ *   q             [B][Hq][D] of q_dtype, 16-byte aligned
+ *   k_pool        [NB][Hkv][16][D] of kv_dtype, 16-byte aligned
+ *   v_pool        [NB][Hkv][D][16] of kv_dtype, 16-byte aligned
+ *   block_tables  int32 [B][max_blocks_per_seq]; entries past
+ *                 ceil(seq_lens[b]/16) are never read (pad freely, e.g. -1)
+ *   seq_lens      int32 [B]: tokens attended, including any token appended
+ *                 for this step; 0 gives an all-zero output row
+ *   scale         multiplier of q.K (usually 1/sqrt(D))
+ *   out           [B][Hq][D] of q_dtype, 16-byte aligned, written entirely
+ *   workspace     device buffer of at least pa_decode_workspace_size(desc)
+ *                 bytes, 256-byte aligned; may be NULL when that size is 0
+ * Two kernels run on `stream`: the main pass (which writes the rows of
+ * sequences handled by a single workgroup) and a merge pass for sequences
+ * whose context was split across workgroups.  Calls that share a workspace
+ * must be ordered on one stream.
+ */
+int pa_decode(const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, const int32_t* seq_lens,
+              float scale, void* out, const pa_decode_desc* desc,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Shapes of one append call.
+ *   num_tokens    N >= 0
+ *   num_kv_heads  Hkv >= 1
+ *   head_size     D in {64, 128, 256}
+ *   block_size    must be 16
+ *   num_blocks    NB >= 1, NB*16 <= INT32_MAX
+ *   kv_dtype      element type of the pools and of k_new / v_new
+ */
+typedef struct {
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t head_size;
+  int32_t block_size;
+  int32_t num_blocks;
+  pa_dtype kv_dtype;
+} pa_append_desc;
+
+/*
+ * KV append: for every i < N with s = slot_mapping[i] in [0, NB*16):
+ *   k_pool[s/16][g][s%16][d] = k_new[i][g][d]
+ *   v_pool[s/16][g][d][s%16] = v_new[i][g][d]     for all g < Hkv, d < D.
+ * A pure byte copy (bit-exact for every dtype).  Negative slots are
+ * skipped.  Slots must be distinct; with duplicates one of the writes wins.
+ * k_new, v_new, k_pool and v_pool must be 16-byte aligned.
+ */
+int pa_kv_append(const void* k_new, const void* v_new,
+                 const int32_t* slot_mapping, void* k_pool, void* v_pool,
+                 const pa_append_desc* desc, void* stream);
+
+/* Static English text of a pa_status value. */
+const char* pa_status_string(int status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

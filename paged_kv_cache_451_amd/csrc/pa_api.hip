@@ -1,0 +1,235 @@
+// C ABI of libpa: argument checks, the split-schedule plan, workspace
+// layout and kernel launches on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+// Resident 64-lane workgroups per compute unit the schedule aims for.
+constexpr int kWavesPerCu = 8;
+// Fewest KV blocks a range should hold before more ranges stop paying off.
+constexpr int kMinBlocksPerRange = 8;
+constexpr int kMaxDevices = 64;
+constexpr size_t kAlign = 256;
+
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return 0;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount,
+                              dev) != hipSuccess || n <= 0)
+      return 0;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t dtype_bytes(pa_dtype t) {
+  switch (t) {
+    case PA_F32: return 4;
+    case PA_BF16: return 2;
+    case PA_FP8_E4M3FN: return 1;
+  }
+  return 0;
+}
+
+bool head_size_ok(int d) { return d == 64 || d == 128 || d == 256; }
+
+int check_desc(const pa_decode_desc* d) {
+  if (!d) return PA_ERR_NULL;
+  if (d->num_seqs < 0 || d->num_seqs > 65536) return PA_ERR_SHAPE;
+  if (d->num_kv_heads < 1 || d->num_q_heads < d->num_kv_heads ||
+      d->num_q_heads % d->num_kv_heads)
+    return PA_ERR_SHAPE;
+  if (!head_size_ok(d->head_size) || d->block_size != pa::kBlock)
+    return PA_ERR_SHAPE;
+  if (d->num_blocks < 1 ||
+      (int64_t)d->num_blocks * pa::kBlock > INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (d->max_blocks_per_seq < 1 || d->max_seq_len < 0) return PA_ERR_SHAPE;
+  // per-head block counts and their prefix sums stay in int32
+  if ((int64_t)d->num_seqs * d->max_blocks_per_seq > INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (d->num_waves < 0 || d->total_blocks_hint < 0) return PA_ERR_SHAPE;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (d->q_dtype == PA_F32 && d->kv_dtype == PA_F32) {
+    if (G > 8) return PA_ERR_SHAPE;
+  } else if (d->q_dtype == PA_BF16 &&
+             (d->kv_dtype == PA_BF16 || d->kv_dtype == PA_FP8_E4M3FN)) {
+    if (G > 16) return PA_ERR_SHAPE;
+  } else {
+    return PA_ERR_DTYPE;
+  }
+  if (d->kv_dtype == PA_FP8_E4M3FN &&
+      !(d->k_scale > 0.f && d->v_scale > 0.f && isfinite(d->k_scale) &&
+        isfinite(d->v_scale)))
+    return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+struct Plan {
+  int Wh;  // ranges per KV head
+  int W;   // workgroups of the main pass
+  size_t off_ml, off_o, bytes;
+};
+
+// Ranges per KV head: enough resident workgroups to fill every CU, but no
+// range shorter than kMinBlocksPerRange blocks when the total is known or
+// bounded.
+bool make_plan(const pa_decode_desc* d, Plan* p) {
+  const int hkv = d->num_kv_heads;
+  const int G = d->num_q_heads / hkv;
+  int64_t wh;
+  if (d->num_waves > 0) {
+    wh = d->num_waves / hkv;
+  } else {
+    const int cus = cu_count();
+    if (cus <= 0) return false;
+    wh = (int64_t)cus * kWavesPerCu / hkv;
+    int64_t units = d->total_blocks_hint;
+    if (units <= 0) {
+      int64_t per = (d->max_seq_len + pa::kBlock - 1) / pa::kBlock;
+      if (per > d->max_blocks_per_seq) per = d->max_blocks_per_seq;
+      units = (int64_t)d->num_seqs * per;
+    }
+    int64_t cap = (units + kMinBlocksPerRange - 1) / kMinBlocksPerRange;
+    if (wh > cap) wh = cap;
+  }
+  if (wh < 1) wh = 1;
+  if (wh * hkv > INT32_MAX / 2) wh = INT32_MAX / 2 / hkv;
+  p->Wh = (int)wh;
+  p->W = (int)(wh * hkv);
+  const size_t rows = (size_t)p->W * 2 * G;
+  const size_t prefix = round_up(((size_t)d->num_seqs + 1) * sizeof(int32_t));
+  p->off_ml = prefix;
+  p->off_o = p->off_ml + round_up(rows * 2 * sizeof(float));
+  p->bytes = p->off_o + round_up(rows * d->head_size * sizeof(float));
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return kAbiVersion; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "success";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_DTYPE: return "unsupported dtype combination";
+    case PA_ERR_SHAPE: return "unsupported or inconsistent size";
+    case PA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_DEVICE: return "no usable HIP device";
+  }
+  return "unknown status";
+}
+
+size_t pa_decode_workspace_size(const pa_decode_desc* desc) {
+  if (check_desc(desc) != PA_OK) return 0;
+  if (desc->num_seqs == 0) return 0;
+  Plan p;
+  if (!make_plan(desc, &p)) return 0;
+  return p.bytes;
+}
+
+int pa_decode(const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, const int32_t* seq_lens,
+              float scale, void* out, const pa_decode_desc* desc,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (desc->num_seqs == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out)
+    return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned16(out) || ((uintptr_t)block_tables & 3u) ||
+      ((uintptr_t)seq_lens & 3u))
+    return PA_ERR_ALIGN;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  Plan p;
+  if (!make_plan(desc, &p)) return PA_ERR_DEVICE;
+  if (!workspace || workspace_bytes < p.bytes) return PA_ERR_WORKSPACE;
+  if ((uintptr_t)workspace % kAlign) return PA_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  pa::DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.out = out;
+  const float k_scale = desc->kv_dtype == PA_FP8_E4M3FN ? desc->k_scale : 1.f;
+  a.c_log2 = (float)((double)scale * 1.4426950408889634 * (double)k_scale);
+  a.v_scale = desc->kv_dtype == PA_FP8_E4M3FN ? desc->v_scale : 1.f;
+  a.Hq = desc->num_q_heads;
+  a.NB = desc->num_blocks;
+  a.s.seq_lens = seq_lens;
+  a.s.block_tables = block_tables;
+  a.s.prefix = reinterpret_cast<int32_t*>(ws);
+  a.s.part_ml = reinterpret_cast<float*>(ws + p.off_ml);
+  a.s.part_o = reinterpret_cast<float*>(ws + p.off_o);
+  a.s.B = desc->num_seqs;
+  a.s.max_blocks = desc->max_blocks_per_seq;
+  a.s.Hkv = desc->num_kv_heads;
+  a.s.G = desc->num_q_heads / desc->num_kv_heads;
+  a.s.Wh = p.Wh;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(
+      const_cast<void**>(desc->profile_events));
+  if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return PA_ERR_LAUNCH;
+  hipError_t e;
+  if (desc->kv_dtype == PA_F32)
+    e = pa::launch_decode_valu(desc->head_size, a, p.W, s);
+  else
+    e = pa::launch_decode_mfma(desc->kv_dtype == PA_FP8_E4M3FN,
+                               desc->head_size, a, p.W, s);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return PA_ERR_LAUNCH;
+  e = pa::launch_decode_merge(desc->q_dtype == PA_BF16, desc->head_size, a,
+                              s);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_kv_append(const void* k_new, const void* v_new,
+                 const int32_t* slot_mapping, void* k_pool, void* v_pool,
+                 const pa_append_desc* desc, void* stream) {
+  if (!desc) return PA_ERR_NULL;
+  if (desc->num_tokens < 0 || desc->num_kv_heads < 1 ||
+      !head_size_ok(desc->head_size) || desc->block_size != pa::kBlock ||
+      desc->num_blocks < 1 ||
+      (int64_t)desc->num_blocks * pa::kBlock > INT32_MAX)
+    return PA_ERR_SHAPE;
+  const size_t eb = dtype_bytes(desc->kv_dtype);
+  if (eb == 0) return PA_ERR_DTYPE;
+  if (desc->num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool)
+    return PA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) ||
+      !aligned16(v_pool) || ((uintptr_t)slot_mapping & 3u))
+    return PA_ERR_ALIGN;
+  hipError_t e = pa::launch_kv_append(
+      (int)eb, k_new, v_new, slot_mapping, k_pool, v_pool, desc->num_tokens,
+      desc->num_kv_heads, desc->head_size, desc->num_blocks,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"

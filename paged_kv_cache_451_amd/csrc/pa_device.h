@@ -1,0 +1,122 @@
+// Device-side helpers shared by the decode kernels of libpa.
+//
+// Work split ("split context"): for every KV head g, the flattened sequence
+// of that head's KV blocks over all sequences (sequence-major, U blocks in
+// total) is cut into Wh equal contiguous ranges, one per 64-lane workgroup.
+// Range k covers blocks [floor(k*U/Wh), floor((k+1)*U/Wh)).  A workgroup
+// walks every sequence that overlaps its range; a sequence wholly inside the
+// range is finished in place (its output row written directly), one that
+// crosses a range boundary leaves a partial (running max m, sum l and
+// unnormalised output o) that the merge kernel combines.  Each workgroup
+// leaves at most two partials: slot 0 for the sequence that started before
+// its range, slot 1 for the one that continues after it.
+//
+// Workgroup w handles KV head g = w % Hkv, range k = w / Hkv; consecutive
+// workgroup ids are dealt round-robin to the 8 XCDs, so with Hkv = 8 every
+// XCD streams a single KV head and its L2 keeps that head's shared blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlock = 16;  // tokens per KV block
+constexpr int kWave = 64;   // lanes per wavefront on gfx950
+
+struct SplitArgs {
+  const int32_t* seq_lens;
+  const int32_t* block_tables;
+  int32_t* prefix;  // [B+1] exclusive prefix of per-sequence block counts
+  float* part_ml;   // [W][2][G][2]  (m in log2 units, l)
+  float* part_o;    // [W][2][G][D]
+  int B;
+  int max_blocks;   // row length of block_tables
+  int Hkv;
+  int G;
+  int Wh;           // ranges (workgroups) per KV head
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Tokens of sequence b that the kernels attend: clamp to the table row.
+__device__ __forceinline__ int clamped_len(const SplitArgs& a, int b) {
+  int L = a.seq_lens[b];
+  int cap = a.max_blocks * kBlock;
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int range_begin(int k, int U, int Wh) {
+  return (int)(((int64_t)k * U) / Wh);
+}
+
+// Range index k holding block u (0 <= u < U).
+__device__ __forceinline__ int range_of(int u, int U, int Wh) {
+  return (int)((((int64_t)u + 1) * Wh + U - 1) / U) - 1;
+}
+
+__device__ __forceinline__ int readlane(int v, int l) {
+  return __builtin_amdgcn_readlane(v, l);
+}
+
+// Total blocks U per head (sum of ceil(len/16)); workgroup 0 also stores the
+// exclusive prefix for the merge kernel.
+__device__ inline int total_blocks(const SplitArgs& a, bool store_prefix) {
+  const int lane = lane_id();
+  int carry = 0;
+  for (int c0 = 0; c0 < a.B; c0 += kWave) {
+    int b = c0 + lane;
+    int nb = b < a.B ? (clamped_len(a, b) + kBlock - 1) / kBlock : 0;
+    int incl = wave_incl_scan(nb) + carry;
+    if (store_prefix && b < a.B) a.prefix[b] = incl - nb;
+    carry = readlane(incl, kWave - 1);
+  }
+  if (store_prefix && lane == 0) a.prefix[a.B] = carry;
+  return carry;
+}
+
+// Calls seg(b, Sb, Sb1) for every sequence b (in order) whose block span
+// [Sb, Sb1) overlaps [u0, u1) and is non-empty.  All arguments are uniform.
+template <typename Seg>
+__device__ inline void for_each_segment(const SplitArgs& a, int u0, int u1,
+                                        Seg&& seg) {
+  const int lane = lane_id();
+  int carry = 0;
+  for (int c0 = 0; c0 < a.B; c0 += kWave) {
+    int b = c0 + lane;
+    int nb = b < a.B ? (clamped_len(a, b) + kBlock - 1) / kBlock : 0;
+    int incl = wave_incl_scan(nb) + carry;
+    int excl = incl - nb;
+    int chunk_end = readlane(incl, kWave - 1);
+    if (chunk_end > u0) {
+      uint64_t mask = __ballot(nb > 0 && excl < u1 && incl > u0);
+      while (mask) {
+        int i = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        seg(c0 + i, readlane(excl, i), readlane(incl, i));
+      }
+    }
+    if (chunk_end >= u1) break;
+    carry = chunk_end;
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+}  // namespace pa

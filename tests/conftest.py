@@ -15,44 +15,7 @@ def pytest_configure(config):
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
-_RAW_VIEW = {
-    torch.float32: (torch.float32, "f32"),
-    torch.bfloat16: (torch.uint16, "bf16"),
-    torch.float8_e4m3fn: (torch.uint8, "fp8_e4m3fn"),
-}
-
-
-def raw(t: torch.Tensor):
-    """Host numpy array of a tensor's storage bits plus its dtype name."""
-    view, name = _RAW_VIEW[t.dtype]
-    return t.detach().cpu().contiguous().view(view).numpy(), name
-
-
-def raw_bits(t: torch.Tensor) -> np.ndarray:
-    """Bytes of a tensor as uint8 (for bit-exact comparisons)."""
-    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
-
-
-def oracle_args(case, k_pool=None, v_pool=None):
-    """Arguments of ``oracle.paged_decode`` for a ``DecodeCase``."""
-    q, q_dtype = raw(case.q)
-    k, kv_dtype = raw(case.k_pool if k_pool is None else k_pool)
-    v, _ = raw(case.v_pool if v_pool is None else v_pool)
-    return dict(q=q, k_raw=k, v_raw=v,
-                block_tables=case.block_tables.numpy(),
-                seq_lens=case.seq_lens.numpy(), scale=case.scale,
-                q_dtype=q_dtype, kv_dtype=kv_dtype,
-                k_scale=case.k_scale, v_scale=case.v_scale)
-
-
-def appended_pools(case):
-    """Raw K/V pools after the oracle's append of the case's new tokens."""
-    import oracle
-    k, _ = raw(case.k_pool)
-    v, _ = raw(case.v_pool)
-    kn, _ = raw(case.k_new)
-    vn, _ = raw(case.v_new)
-    return oracle.kv_append(k, v, kn, vn, case.slot_mapping.numpy())
+from oracle.adapters import appended_pools, oracle_args, raw, raw_bits  # noqa: E402,F401
 
 
 @pytest.fixture(scope="session")
