@@ -173,7 +173,8 @@ def test_dominant_key_probe_reads_the_right_token(gpu_lib, name):
     tab = case.block_tables.numpy()
     qdt = case.q.dtype
     case.q = torch.ones_like(case.q, dtype=torch.float32).to(qdt)
-    hot_val = 8.0 if case.config.kv_dtype == "fp8_e4m3fn" else 4.0
+    # a real K value of 4 along q: fp8 pools store value / k_scale
+    hot_val = min(448.0, 4.0 / case.k_scale)
     hot = {}
     kp = case.k_pool.clone()
     picks = [0, 15, 16, 31, 32, 47]
@@ -265,8 +266,6 @@ EDGE = [
 @pytest.mark.parametrize("waves", [0, 1, 4096])
 def test_edge_shapes(gpu_lib, spec, waves):
     case = _custom_case(**spec)
-    if case.config.kv_dtype == "fp8_e4m3fn":
-        pass
     nw = waves * case.config.num_kv_heads if waves else 0
     out, _ = run_step(gpu_lib, case, num_waves=nw)
     err = max_err(out, oracle_out(case))
