@@ -86,14 +86,15 @@ def cpu_baseline(case, budget_s: float):
     args.update(k_raw=kp, v_raw=vp)
     lens = case.seq_lens.numpy()
     done, t_total, tokens = [], 0.0, 0
-    for i in range(len(lens)):
-        t0 = time.perf_counter()
-        oracle.paged_decode(**args, seqs=[i])
-        t_total += time.perf_counter() - t0
-        done.append(i)
-        tokens += int(lens[i])
-        if t_total >= budget_s:
-            break
+    while t_total < budget_s:
+        for i in range(len(lens)):
+            t0 = time.perf_counter()
+            oracle.paged_decode(**args, seqs=[i])
+            t_total += time.perf_counter() - t0
+            done.append(i)
+            tokens += int(lens[i])
+            if t_total >= budget_s:
+                break
     s_kv = DTYPE_BYTES[cfg.kv_dtype]
     kv_bytes = tokens * cfg.num_kv_heads * cfg.head_size * 2 * s_kv
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -102,8 +103,9 @@ def cpu_baseline(case, budget_s: float):
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle over the first {len(done)} of "
-                   f"{len(lens)} sequences ({tokens} context tokens, "
+        "sample": (f"float64 numpy oracle, {len(done)} sequence decodes "
+                   f"taken in order (cycling) from the {len(lens)} sequences "
+                   f"of this workload ({tokens} context tokens, "
                    f"{t_total:.1f} s); KV bytes read per second"),
         "context_tokens_per_s": round(tokens / t_total, 1),
         "decode_tokens_per_s": round(len(done) / t_total, 3),
@@ -155,7 +157,7 @@ def main():
     out = torch.empty_like(q)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-          for _ in range(a.steps)]
+          for _ in range(max(a.steps, 2 * nrot))]
     stream = torch.cuda.current_stream()
     for pair in ev:  # create the underlying HIP events
         for e in pair:
@@ -171,26 +173,38 @@ def main():
 
     base_desc = desc_for()
     ws = _lib.alloc_workspace(base_desc, dev)
-    descs = [desc_for((e0.cuda_event, e1.cuda_event)) for e0, e1 in ev]
 
-    def step(i, desc):
+    def prepared(i, desc):
         kp, vp = kps[i % nrot], vps[i % nrot]
-        _lib.pa_kv_append(k_new, v_new, slots, kp, vp)
-        _lib.pa_decode(q, kp, vp, tables, lens, case.scale, out,
-                       max_seq_len=case.max_seq_len, workspace=ws, desc=desc)
+        return _lib.PreparedStep(q, kp, vp, tables, lens, case.scale, out,
+                                 desc, ws, k_new, v_new, slots)
 
-    for i in range(a.warmup):
-        step(i, base_desc)
+    warm = [prepared(i, base_desc) for i in range(a.warmup)]
+    timed = [prepared(a.warmup + i, base_desc) for i in range(a.steps)]
+    for step in warm:
+        step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({a.warmup} steps, {nrot} pool copies)",
           file=sys.stderr, flush=True)
 
+    # the timed region: K whole steps back to back, nothing else on the stream
     t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(a.warmup + i, descs[i])
+    for step in timed:
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / a.steps
+
+    # the dominant kernel alone: HIP events recorded on the launch stream
+    # right before and after each main decode kernel (events serialise the
+    # stream, so this runs as its own region after the timed one)
+    roof = [_lib.PreparedStep(q, kps[i % nrot], vps[i % nrot], tables, lens,
+                              case.scale, out,
+                              desc_for((e0.cuda_event, e1.cuda_event)), ws)
+            for i, (e0, e1) in enumerate(ev)]
+    for step in roof:
+        step()
+    torch.cuda.synchronize()
     kern_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     kern_ms.sort()
     k_avg = sum(kern_ms) / len(kern_ms)

@@ -174,3 +174,38 @@ def pa_kv_append(k_new, v_new, slot_mapping, k_pool, v_pool) -> None:
     _check(lib.pa_kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
                             _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
                             _stream()))
+
+
+class PreparedStep:
+    """A decode step (append, then decode) with its C arguments marshalled
+    once, for replaying the same call many times (benchmarks, serving loops).
+    Holds references to every tensor it points at."""
+
+    def __init__(self, q, k_pool, v_pool, block_tables, seq_lens, scale, out,
+                 desc: DecodeDesc, workspace: torch.Tensor,
+                 k_new=None, v_new=None, slot_mapping=None):
+        lib = load()
+        self._keep = (q, k_pool, v_pool, block_tables, seq_lens, out,
+                      workspace, k_new, v_new, slot_mapping, desc)
+        stream = _stream()
+        self._decode = lib.pa_decode
+        self._decode_args = (
+            _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+            _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
+            ctypes.byref(desc), _ptr(workspace), workspace.numel(), stream)
+        self._append = None
+        if k_new is not None:
+            n, hkv, d = k_new.shape
+            self._adesc = AppendDesc(
+                num_tokens=n, num_kv_heads=hkv, head_size=d,
+                block_size=k_pool.shape[2], num_blocks=k_pool.shape[0],
+                kv_dtype=_DTYPE[k_pool.dtype])
+            self._append = lib.pa_kv_append
+            self._append_args = (
+                _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_pool),
+                _ptr(v_pool), ctypes.byref(self._adesc), stream)
+
+    def __call__(self) -> None:
+        if self._append is not None:
+            _check(self._append(*self._append_args))
+        _check(self._decode(*self._decode_args))

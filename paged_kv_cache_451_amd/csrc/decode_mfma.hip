@@ -23,15 +23,23 @@
 //   A = V^T rows: since V is stored [D][16 tokens] per block and head, lane
 //   (m, j) loads the same 8 tokens of row d = 16*X + m as 16 contiguous
 //   bytes (8 for fp8).  No data moves between lanes except the per-head
-//   max/sum reductions of the online softmax (xor 16 and xor 32).
+//   max reduction of the online softmax (xor 16 and xor 32).
+//
+// The loop is software-pipelined over pairs: the K/V loads of pair i+1 and
+// the block-table entries of pair i+2 are issued before pair i is computed,
+// so each wave keeps a pair (16 KiB of bf16) in flight while it works.  The
+// loads sit outside any branch so the compiler's wait before pair i's math
+// leaves pair i+1's loads outstanding.  fp8 bytes stay raw in registers
+// until their pair is computed.
 //
 // The softmax is the usual online one in base 2: scores are scaled by
 // scale*log2(e) (times k_scale for fp8), a running max m and sum l are kept
-// per head and the accumulator is rescaled when m grows.  P is rounded to
-// bf16 for the matrix core; l sums the rounded values, so the weights used
-// for V sum exactly to the normaliser.  fp8 e4m3fn codes widen exactly to
-// bf16 (v_cvt_pk_f32_fp8 then v_cvt_pk_bf16_f32); k_scale is folded into the
-// score scale and v_scale into the output.
+// per head and the accumulator is rescaled when m grows (skipped when no
+// head's max changed).  P is rounded to bf16 for the matrix core; l sums the
+// rounded values, so the weights applied to V sum exactly to the
+// normaliser.  fp8 e4m3fn codes widen exactly to bf16 (v_cvt_pk_f32_fp8 then
+// v_cvt_pk_bf16_f32); k_scale is folded into the score scale and v_scale
+// into the output.
 //
 // Masking: tokens at or past seq_len, the second block of a pair that lies
 // outside the range, and out-of-range block ids contribute nothing: their
@@ -57,8 +65,9 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 // 8 fp8 e4m3fn codes (little-endian bytes of w) -> 8 bf16, exact.
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(unsigned w0, unsigned w1) {
   bf16x8 r;
+  const unsigned w[2] = {w0, w1};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[h], false);
@@ -83,103 +92,165 @@ __device__ __forceinline__ bf16x8 keep_first(bf16x8 v, int nv) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// Storage-type specific loads.  For bf16 a K row chunk for MFMA c is the 8
-// values at d = 32c + 8j; for fp8 one 16-byte load at d = 64c' + 16j feeds
-// MFMAs 2c' (low 8 bytes) and 2c'+1 (high 8 bytes).  Q uses the same d sets.
-template <bool FP8>
-struct Kv;
+// Raw block-table entries of the pair starting at logical block `blk`.  The
+// indices are clamped to the segment's last block hi - 1, so the loads are
+// always in bounds and need no branch; a pair past the segment end reads a
+// block that was just streamed (an L2 hit) and is never computed.
+struct RawIds {
+  int e0, e1;
+};
 
-template <>
-struct Kv<false> {
+__device__ __forceinline__ RawIds raw_ids(const int32_t* __restrict__ trow,
+                                          int blk, int hi) {
+  const int last = hi - 1;
+  return RawIds{trow[blk < last ? blk : last],
+                trow[blk + 1 < last ? blk + 1 : last]};
+}
+
+// Physical ids to read, made safe: an id outside [0, NB) becomes block 0.
+__device__ __forceinline__ int safe_id(int p, int NB) {
+  return (unsigned)p < (unsigned)NB ? p : 0;
+}
+
+// Valid tokens of the two blocks of the pair at `blk` (uniform).
+__device__ __forceinline__ void pair_valid(const RawIds& r, int blk, int hi,
+                                           int L, int NB, int& nv0,
+                                           int& nv1) {
+  const bool ok0 = (unsigned)r.e0 < (unsigned)NB;
+  const bool ok1 = blk + 1 < hi && (unsigned)r.e1 < (unsigned)NB;
+  const int a = L - blk * kBlock;
+  const int b = a - kBlock;
+  nv0 = ok0 ? (a > kBlock ? kBlock : a) : 0;
+  nv1 = ok1 ? (b > kBlock ? kBlock : (b < 0 ? 0 : b)) : 0;
+}
+
+// Storage-type specific register sets of one pair.  bf16: K chunk c of a row
+// is the 8 values at d = 32c + 8j; fp8: one 16-byte load at d = 64c' + 16j
+// feeds MFMAs 2c' (low 8 bytes) and 2c'+1 (high 8 bytes).  Q uses the same d
+// sets (qcol).
+template <bool FP8, int D>
+struct Pair;
+
+template <int D>
+struct Pair<false, D> {
   typedef __bf16 T;
-  static constexpr int kColJ = 8;  // element offset of k-group j in a row
+  static constexpr int NC = D / 32, NX = D / 16, kColJ = 8;
+  bf16x8 k[2][NC];
+  bf16x8 v[NX];
   __device__ static __forceinline__ int qcol(int c, int j) {
     return 32 * c + 8 * j;
   }
-  template <int D>
-  __device__ static __forceinline__ void load_k(const T* p, bf16x8* k) {
+  __device__ __forceinline__ void load(const T* kl, const T* vl) {
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      k[c] = *reinterpret_cast<const bf16x8*>(p + 32 * c);
-  }
-  template <int D>
-  __device__ static __forceinline__ void load_v(const T* p, bf16x8* v) {
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int x = 0; x < D / 16; ++x)
-      v[x] = *reinterpret_cast<const bf16x8*>(p + 256 * x);
+      for (int c = 0; c < NC; ++c)
+        k[s][c] = *reinterpret_cast<const bf16x8*>(kl + 4 * D * s + 32 * c);
+#pragma unroll
+    for (int x = 0; x < NX; ++x)
+      v[x] = *reinterpret_cast<const bf16x8*>(vl + 256 * x);
   }
+  __device__ __forceinline__ bf16x8 kop(int s, int c) const { return k[s][c]; }
+  __device__ __forceinline__ bf16x8 vop(int x) const { return v[x]; }
 };
 
-template <>
-struct Kv<true> {
+template <int D>
+struct Pair<true, D> {
   typedef uint8_t T;
-  static constexpr int kColJ = 16;
+  static constexpr int NC = D / 32, NX = D / 16, kColJ = 16;
+  u32x4 k[2][D / 64];
+  u32x2 v[NX];
   __device__ static __forceinline__ int qcol(int c, int j) {
     return 64 * (c >> 1) + 16 * j + 8 * (c & 1);
   }
-  template <int D>
-  __device__ static __forceinline__ void load_k(const T* p, bf16x8* k) {
+  __device__ __forceinline__ void load(const T* kl, const T* vl) {
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(p + 64 * c);
-      k[2 * c] = fp8x8_to_bf16(u32x2{w[0], w[1]});
-      k[2 * c + 1] = fp8x8_to_bf16(u32x2{w[2], w[3]});
-    }
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c)
+        k[s][c] = *reinterpret_cast<const u32x4*>(kl + 4 * D * s + 64 * c);
+#pragma unroll
+    for (int x = 0; x < NX; ++x)
+      v[x] = *reinterpret_cast<const u32x2*>(vl + 256 * x);
   }
-  template <int D>
-  __device__ static __forceinline__ void load_v(const T* p, bf16x8* v) {
-#pragma unroll
-    for (int x = 0; x < D / 16; ++x)
-      v[x] = fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(p + 256 * x));
+  __device__ __forceinline__ bf16x8 kop(int s, int c) const {
+    const u32x4 w = k[s][c >> 1];
+    return (c & 1) ? fp8x8_to_bf16(w[2], w[3]) : fp8x8_to_bf16(w[0], w[1]);
+  }
+  __device__ __forceinline__ bf16x8 vop(int x) const {
+    return fp8x8_to_bf16(v[x][0], v[x][1]);
   }
 };
 
-template <bool FP8, int D>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
-  typedef Kv<FP8> KV;
-  typedef typename KV::T T;
-  constexpr int NC = D / 32;  // QK MFMAs per 16 tokens
-  constexpr int NX = D / 16;  // PV MFMAs (16-row tiles of d)
+// Minimum resident waves per SIMD the register budget is held to.
+template <int D>
+constexpr int min_waves() { return D > 128 ? 1 : 2; }
 
-  const SplitArgs& s = a.s;
+template <bool FP8, int D>
+__global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
+    const __bf16* __restrict__ q, const void* __restrict__ k_pool,
+    const void* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ seq_lens, __bf16* __restrict__ out,
+    int32_t* __restrict__ prefix, float* __restrict__ part_ml,
+    float* __restrict__ part_o, Sched sc) {
+  typedef Pair<FP8, D> P;
+  typedef typename P::T T;
+  constexpr int NC = P::NC;
+  constexpr int NX = P::NX;
+
   const int lane = threadIdx.x;
   const int r16 = lane & 15;
   const int j = lane >> 4;
   const int w = blockIdx.x;
-  const int g = w % s.Hkv;
-  const int k = w / s.Hkv;
-  const int G = s.G;
+  const int g = w % sc.Hkv;
+  const int k = w / sc.Hkv;
+  const int G = sc.G;
 
-  const int U = total_blocks(s, w == 0);
-  const int u0 = range_begin(k, U, s.Wh);
-  const int u1 = range_begin(k + 1, U, s.Wh);
+  const int U = total_blocks(seq_lens, sc.B, sc.max_blocks,
+                             w == 0 ? prefix : nullptr);
+  const int u0 = range_begin(k, U, sc.Wh);
+  const int u1 = range_begin(k + 1, U, sc.Wh);
   if (u0 >= u1) return;
 
-  const T* kpool = reinterpret_cast<const T*>(a.k_pool);
-  const T* vpool = reinterpret_cast<const T*>(a.v_pool);
+  const T* kpool = reinterpret_cast<const T*>(k_pool);
+  const T* vpool = reinterpret_cast<const T*>(v_pool);
   const size_t tile = (size_t)kBlock * D;  // elements of one (block, head) tile
+  const size_t gtile = (size_t)g * tile;
+  const size_t btile = (size_t)sc.Hkv * tile;
   // lane-constant parts of the K and V addresses
-  const int k_lane = (((r16 >> 2) & 1) * 8 + (r16 & 3)) * D + KV::kColJ * j;
+  const int k_lane = (((r16 >> 2) & 1) * 8 + (r16 & 3)) * D + P::kColJ * j;
   const int v_lane = r16 * kBlock + 8 * (j & 1);
   const bool k_hi = r16 >= 8;  // K row from the pair's second block
   const bool v_hi = j >= 2;    // V tokens from the pair's second block
 
-  for_each_segment(s, u0, u1, [&](int b, int Sb, int Sb1) {
-    const int L = clamped_len(s, b);
+  for_each_segment(seq_lens, sc.B, sc.max_blocks, u0, u1,
+                   [&](int b, int Sb, int Sb1) {
+    const int L = clamp_len(seq_lens[b], sc.max_blocks);
     const int lo = (Sb > u0 ? Sb : u0) - Sb;
     const int hi = (Sb1 < u1 ? Sb1 : u1) - Sb;
-    const int32_t* trow = s.block_tables + (size_t)b * s.max_blocks;
+    const int32_t* trow = block_tables + (size_t)b * sc.max_blocks;
+
+    auto issue = [&](P& pr, const RawIds& id) {
+      const size_t base0 = (size_t)safe_id(id.e0, sc.NB) * btile + gtile;
+      const size_t base1 = (size_t)safe_id(id.e1, sc.NB) * btile + gtile;
+      pr.load(kpool + (k_hi ? base1 : base0) + k_lane,
+              vpool + (v_hi ? base1 : base0) + v_lane);
+    };
+
+    RawIds ia = raw_ids(trow, lo, hi);
+    P A, B;
+    issue(A, ia);
+    RawIds ib = raw_ids(trow, lo + 2, hi);
 
     // Q as the B operand of QK: lane (n, j) holds head g*G + n.
     bf16x8 qb[NC];
     {
       const int n = r16;
-      const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) +
-                           ((size_t)b * a.Hq + (size_t)g * G + n) * D;
+      const __bf16* qrow = q + ((size_t)b * sc.Hq + (size_t)g * G + n) * D;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         bf16x8 z = {};
-        qb[c] = n < G ? *reinterpret_cast<const bf16x8*>(qrow + KV::qcol(c, j))
+        qb[c] = n < G ? *reinterpret_cast<const bf16x8*>(qrow + P::qcol(c, j))
                       : z;
       }
     }
@@ -190,56 +261,33 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     float m = -INFINITY;
     float lsum = 0.f;
 
-    for (int blk = lo; blk < hi; blk += 2) {
-      const bool has1 = blk + 1 < hi;
-      int p0 = trow[blk];
-      int p1 = has1 ? trow[blk + 1] : p0;
-      int nv0 = (unsigned)p0 < (unsigned)a.NB ? L - blk * kBlock : 0;
-      int nv1 = has1 && (unsigned)p1 < (unsigned)a.NB
-                    ? L - (blk + 1) * kBlock : 0;
-      nv0 = nv0 > kBlock ? kBlock : nv0;
-      nv1 = nv1 > kBlock ? kBlock : (nv1 < 0 ? 0 : nv1);
-      if ((unsigned)p0 >= (unsigned)a.NB) p0 = 0;
-      if ((unsigned)p1 >= (unsigned)a.NB) p1 = p0;
-
-      const size_t base0 = ((size_t)p0 * s.Hkv + g) * tile;
-      const size_t base1 = ((size_t)p1 * s.Hkv + g) * tile;
-      const T* kl = kpool + (k_hi ? base1 : base0) + k_lane;
-      const T* vl = vpool + (v_hi ? base1 : base0) + v_lane;
-
-      bf16x8 kr0[NC], kr1[NC], vr[NX];
-      KV::template load_k<D>(kl, kr0);
-      KV::template load_k<D>(kl + 4 * D, kr1);
-      KV::template load_v<D>(vl, vr);
-
+    auto compute = [&](const P& pr, const RawIds& id, int blk) {
+      int nv0, nv1;
+      pair_valid(id, blk, hi, L, sc.NB, nv0, nv1);
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        s0 = mfma16x16x32(kr0[c], qb[c], s0);
-        s1 = mfma16x16x32(kr1[c], qb[c], s1);
+        s0 = mfma16x16x32(pr.kop(0, c), qb[c], s0);
+        s1 = mfma16x16x32(pr.kop(1, c), qb[c], s1);
       }
-
-      // this lane's 8 tokens: 8*(j%2) + e of block j/2
-      const int nvb = v_hi ? nv1 : nv0;
-      int nv = nvb - 8 * (j & 1);
-      nv = nv < 0 ? 0 : (nv > 8 ? 8 : nv);
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = s0[i] * a.c_log2;
-        x[4 + i] = s1[i] * a.c_log2;
+        x[i] = s0[i] * sc.c_log2;
+        x[4 + i] = s1[i] * sc.c_log2;
       }
-      if (nv0 + nv1 < 2 * kBlock) {
+      // this lane's 8 tokens: 8*(j%2) + e of block j/2
+      const bool partial = nv0 + nv1 < 2 * kBlock;
+      int nv = (v_hi ? nv1 : nv0) - 8 * (j & 1);
+      nv = nv < 0 ? 0 : (nv > 8 ? 8 : nv);
+      if (partial) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = e < nv ? x[e] : -INFINITY;
-#pragma unroll
-        for (int xx = 0; xx < NX; ++xx) vr[xx] = keep_first(vr[xx], nv);
       }
-      float mx = x[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);
+      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);
       const float m_new = fmaxf(m, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fast_exp2(m - m_use);
@@ -247,17 +295,40 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        __bf16 pe = (__bf16)fast_exp2(x[e] - m_use);
+        const __bf16 pe = (__bf16)fast_exp2(x[e] - m_use);
         pb[e] = pe;
         psum += (float)pe;
       }
       lsum = lsum * alpha + psum;
       m = m_new;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int xx = 0; xx < NX; ++xx) acc[xx] *= alpha;
+      }
 #pragma unroll
       for (int xx = 0; xx < NX; ++xx) {
-        acc[xx] *= alpha;
-        acc[xx] = mfma16x16x32(vr[xx], pb, acc[xx]);
+        bf16x8 vv = pr.vop(xx);
+        if (partial) vv = keep_first(vv, nv);
+        acc[xx] = mfma16x16x32(vv, pb, acc[xx]);
       }
+    };
+
+    // Loop invariant: A holds the loads of pair blk, ib the table entries of
+    // pair blk + 2.  Loads are issued unconditionally (see raw_ids).
+    int blk = lo;
+    for (;;) {
+      issue(B, ib);
+      RawIds ic = raw_ids(trow, blk + 4, hi);
+      compute(A, ia, blk);
+      blk += 2;
+      if (blk >= hi) break;
+      issue(A, ic);
+      RawIds id = raw_ids(trow, blk + 4, hi);
+      compute(B, ib, blk);
+      blk += 2;
+      if (blk >= hi) break;
+      ia = ic;
+      ib = id;
     }
 
     // lane (n, j) holds O[head n][16X + 4j + i]
@@ -267,9 +338,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     if (n < G) {
       const bool split = Sb < u0 || Sb1 > u1;
       if (!split) {
-        const float inv = ltot > 0.f ? a.v_scale / ltot : 0.f;
-        __bf16* orow = reinterpret_cast<__bf16*>(a.out) +
-                       ((size_t)b * a.Hq + (size_t)g * G + n) * D + 4 * j;
+        const float inv = ltot > 0.f ? sc.v_scale / ltot : 0.f;
+        __bf16* orow = out + ((size_t)b * sc.Hq + (size_t)g * G + n) * D +
+                       4 * j;
 #pragma unroll
         for (int xx = 0; xx < NX; ++xx) {
           bf16x4 o;
@@ -280,42 +351,65 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       } else {
         const int slot = Sb < u0 ? 0 : 1;
         const size_t row = ((size_t)w * 2 + slot) * G + n;
-        float* po = s.part_o + row * D + 4 * j;
+        float* po = part_o + row * D + 4 * j;
 #pragma unroll
         for (int xx = 0; xx < NX; ++xx)
-          *reinterpret_cast<f32x4*>(po + 16 * xx) = acc[xx] * a.v_scale;
+          *reinterpret_cast<f32x4*>(po + 16 * xx) = acc[xx] * sc.v_scale;
         if (j == 0) {
-          s.part_ml[row * 2 + 0] = m;
-          s.part_ml[row * 2 + 1] = ltot;
+          part_ml[row * 2 + 0] = m;
+          part_ml[row * 2 + 1] = ltot;
         }
       }
     }
   });
 }
 
+template <bool FP8, int D>
+void launch_one(const DecodeArgs& a, int nwg, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_mfma_kernel<FP8, D>), dim3(nwg), dim3(64), 0,
+                     stream, reinterpret_cast<const __bf16*>(a.q), a.k_pool,
+                     a.v_pool, a.block_tables, a.seq_lens,
+                     reinterpret_cast<__bf16*>(a.out), a.prefix, a.part_ml,
+                     a.part_o, a.s);
+}
+
+template <bool FP8, int D>
+int occupancy_one() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(decode_mfma_kernel<FP8, D>), 64,
+          0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+template <bool FP8>
+int occupancy_d(int head_size) {
+  switch (head_size) {
+    case 64: return occupancy_one<FP8, 64>();
+    case 128: return occupancy_one<FP8, 128>();
+    case 256: return occupancy_one<FP8, 256>();
+  }
+  return 0;
+}
+
 template <bool FP8>
 hipError_t launch_d(int head_size, const DecodeArgs& a, int nwg,
                     hipStream_t stream) {
   switch (head_size) {
-    case 64:
-      hipLaunchKernelGGL((decode_mfma_kernel<FP8, 64>), dim3(nwg), dim3(64),
-                         0, stream, a);
-      break;
-    case 128:
-      hipLaunchKernelGGL((decode_mfma_kernel<FP8, 128>), dim3(nwg), dim3(64),
-                         0, stream, a);
-      break;
-    case 256:
-      hipLaunchKernelGGL((decode_mfma_kernel<FP8, 256>), dim3(nwg), dim3(64),
-                         0, stream, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 64: launch_one<FP8, 64>(a, nwg, stream); break;
+    case 128: launch_one<FP8, 128>(a, nwg, stream); break;
+    case 256: launch_one<FP8, 256>(a, nwg, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+int occupancy_decode_mfma(bool fp8, int head_size) {
+  return fp8 ? occupancy_d<true>(head_size) : occupancy_d<false>(head_size);
+}
 
 hipError_t launch_decode_mfma(bool fp8, int head_size, const DecodeArgs& a,
                               int nwg, hipStream_t stream) {

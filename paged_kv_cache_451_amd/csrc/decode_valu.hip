@@ -26,39 +26,42 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMaxG = 8;
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_valu_kernel(
+    const float* __restrict__ q, const float* __restrict__ kpool,
+    const float* __restrict__ vpool, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ out,
+    int32_t* __restrict__ prefix, float* __restrict__ part_ml,
+    float* __restrict__ part_o, Sched sc) {
   constexpr int DQ = D / 4;   // K values per lane (a quarter row)
   constexpr int NR = D / 64;  // output columns per lane
   __shared__ float qs[kMaxG][D];
   __shared__ float ps[kMaxG][kBlock];
 
-  const SplitArgs& s = a.s;
   const int lane = threadIdx.x;
   const int t = lane & 15;
   const int j = lane >> 4;
   const int w = blockIdx.x;
-  const int g = w % s.Hkv;
-  const int k = w / s.Hkv;
-  const int G = s.G;
+  const int g = w % sc.Hkv;
+  const int k = w / sc.Hkv;
+  const int G = sc.G;
 
-  const int U = total_blocks(s, w == 0);
-  const int u0 = range_begin(k, U, s.Wh);
-  const int u1 = range_begin(k + 1, U, s.Wh);
+  const int U = total_blocks(seq_lens, sc.B, sc.max_blocks,
+                             w == 0 ? prefix : nullptr);
+  const int u0 = range_begin(k, U, sc.Wh);
+  const int u1 = range_begin(k + 1, U, sc.Wh);
   if (u0 >= u1) return;
 
-  const float* kpool = reinterpret_cast<const float*>(a.k_pool);
-  const float* vpool = reinterpret_cast<const float*>(a.v_pool);
   const size_t tile = (size_t)kBlock * D;
 
-  for_each_segment(s, u0, u1, [&](int b, int Sb, int Sb1) {
-    const int L = clamped_len(s, b);
+  for_each_segment(seq_lens, sc.B, sc.max_blocks, u0, u1,
+                   [&](int b, int Sb, int Sb1) {
+    const int L = clamp_len(seq_lens[b], sc.max_blocks);
     const int lo = (Sb > u0 ? Sb : u0) - Sb;
     const int hi = (Sb1 < u1 ? Sb1 : u1) - Sb;
-    const int32_t* trow = s.block_tables + (size_t)b * s.max_blocks;
+    const int32_t* trow = block_tables + (size_t)b * sc.max_blocks;
 
     __syncthreads();
-    const float* qrow = reinterpret_cast<const float*>(a.q) +
-                        ((size_t)b * a.Hq + (size_t)g * G) * D;
+    const float* qrow = q + ((size_t)b * sc.Hq + (size_t)g * G) * D;
     for (int i = lane; i < G * D; i += kWave) qs[i / D][i % D] = qrow[i];
     __syncthreads();
 
@@ -74,10 +77,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
 
     for (int blk = lo; blk < hi; ++blk) {
       int p = trow[blk];
-      int nv = (unsigned)p < (unsigned)a.NB ? L - blk * kBlock : 0;
+      int nv = (unsigned)p < (unsigned)sc.NB ? L - blk * kBlock : 0;
       nv = nv > kBlock ? kBlock : nv;
-      if ((unsigned)p >= (unsigned)a.NB) p = 0;
-      const size_t base = ((size_t)p * s.Hkv + g) * tile;
+      if ((unsigned)p >= (unsigned)sc.NB) p = 0;
+      const size_t base = ((size_t)p * sc.Hkv + g) * tile;
 
       float kr[DQ];
       const float* kp = kpool + base + (size_t)t * D + j * DQ;
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
         for (int i = 0; i < DQ; ++i) dot = fmaf(qs[n][j * DQ + i], kr[i], dot);
         dot += __shfl_xor(dot, 16, kWave);
         dot += __shfl_xor(dot, 32, kWave);
-        float x = t < nv ? dot * a.c_log2 : -INFINITY;
+        float x = t < nv ? dot * sc.c_log2 : -INFINITY;
         float mx = x;
 #pragma unroll
         for (int o2 = 1; o2 < 16; o2 <<= 1) mx = wave_max_xor(mx, o2);
@@ -143,9 +146,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
     for (int n = 0; n < kMaxG; ++n) {
       if (n >= G) break;
       if (!split) {
-        const float inv = l[n] > 0.f ? a.v_scale / l[n] : 0.f;
-        float* orow = reinterpret_cast<float*>(a.out) +
-                      ((size_t)b * a.Hq + (size_t)g * G + n) * D;
+        const float inv = l[n] > 0.f ? sc.v_scale / l[n] : 0.f;
+        float* orow = out + ((size_t)b * sc.Hq + (size_t)g * G + n) * D;
 #pragma unroll
         for (int r = 0; r < NR; ++r) orow[lane + 64 * r] = o[n][r] * inv;
       } else {
@@ -153,35 +155,54 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
         const size_t row = ((size_t)w * 2 + slot) * G + n;
 #pragma unroll
         for (int r = 0; r < NR; ++r)
-          s.part_o[row * D + lane + 64 * r] = o[n][r] * a.v_scale;
+          part_o[row * D + lane + 64 * r] = o[n][r] * sc.v_scale;
         if (lane == 0) {
-          s.part_ml[row * 2 + 0] = m[n];
-          s.part_ml[row * 2 + 1] = l[n];
+          part_ml[row * 2 + 0] = m[n];
+          part_ml[row * 2 + 1] = l[n];
         }
       }
     }
   });
 }
 
+template <int D>
+void launch_one(const DecodeArgs& a, int nwg, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_valu_kernel<D>, dim3(nwg), dim3(64), 0, stream,
+                     reinterpret_cast<const float*>(a.q),
+                     reinterpret_cast<const float*>(a.k_pool),
+                     reinterpret_cast<const float*>(a.v_pool), a.block_tables,
+                     a.seq_lens, reinterpret_cast<float*>(a.out), a.prefix,
+                     a.part_ml, a.part_o, a.s);
+}
+
+template <int D>
+int occupancy_one() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(decode_valu_kernel<D>), 64, 0) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+
 }  // namespace
+
+int occupancy_decode_valu(int head_size) {
+  switch (head_size) {
+    case 64: return occupancy_one<64>();
+    case 128: return occupancy_one<128>();
+    case 256: return occupancy_one<256>();
+  }
+  return 0;
+}
 
 hipError_t launch_decode_valu(int head_size, const DecodeArgs& a, int nwg,
                               hipStream_t stream) {
   switch (head_size) {
-    case 64:
-      hipLaunchKernelGGL(decode_valu_kernel<64>, dim3(nwg), dim3(64), 0,
-                         stream, a);
-      break;
-    case 128:
-      hipLaunchKernelGGL(decode_valu_kernel<128>, dim3(nwg), dim3(64), 0,
-                         stream, a);
-      break;
-    case 256:
-      hipLaunchKernelGGL(decode_valu_kernel<256>, dim3(nwg), dim3(64), 0,
-                         stream, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 64: launch_one<64>(a, nwg, stream); break;
+    case 128: launch_one<128>(a, nwg, stream); break;
+    case 256: launch_one<256>(a, nwg, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -12,7 +12,8 @@
 namespace {
 
 constexpr int kAbiVersion = 1;
-// Resident 64-lane workgroups per compute unit the schedule aims for.
+// Upper bound on resident 64-lane workgroups per compute unit the schedule
+// aims for; the kernel's register budget may allow fewer.
 constexpr int kWavesPerCu = 8;
 // Fewest KV blocks a range should hold before more ranges stop paying off.
 constexpr int kMinBlocksPerRange = 8;
@@ -100,7 +101,13 @@ bool make_plan(const pa_decode_desc* d, Plan* p) {
   } else {
     const int cus = cu_count();
     if (cus <= 0) return false;
-    wh = (int64_t)cus * kWavesPerCu / hkv;
+    int per_cu = d->kv_dtype == PA_F32
+                     ? pa::occupancy_decode_valu(d->head_size)
+                     : pa::occupancy_decode_mfma(
+                           d->kv_dtype == PA_FP8_E4M3FN, d->head_size);
+    if (per_cu <= 0) return false;
+    if (per_cu > kWavesPerCu) per_cu = kWavesPerCu;
+    wh = (int64_t)cus * per_cu / hkv;
     int64_t units = d->total_blocks_hint;
     if (units <= 0) {
       int64_t per = (d->max_seq_len + pa::kBlock - 1) / pa::kBlock;
@@ -174,17 +181,17 @@ int pa_decode(const void* q, const void* k_pool, const void* v_pool,
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
   a.out = out;
+  a.prefix = reinterpret_cast<int32_t*>(ws);
+  a.part_ml = reinterpret_cast<float*>(ws + p.off_ml);
+  a.part_o = reinterpret_cast<float*>(ws + p.off_o);
   const float k_scale = desc->kv_dtype == PA_FP8_E4M3FN ? desc->k_scale : 1.f;
-  a.c_log2 = (float)((double)scale * 1.4426950408889634 * (double)k_scale);
-  a.v_scale = desc->kv_dtype == PA_FP8_E4M3FN ? desc->v_scale : 1.f;
-  a.Hq = desc->num_q_heads;
-  a.NB = desc->num_blocks;
-  a.s.seq_lens = seq_lens;
-  a.s.block_tables = block_tables;
-  a.s.prefix = reinterpret_cast<int32_t*>(ws);
-  a.s.part_ml = reinterpret_cast<float*>(ws + p.off_ml);
-  a.s.part_o = reinterpret_cast<float*>(ws + p.off_o);
+  a.s.c_log2 = (float)((double)scale * 1.4426950408889634 * (double)k_scale);
+  a.s.v_scale = desc->kv_dtype == PA_FP8_E4M3FN ? desc->v_scale : 1.f;
+  a.s.Hq = desc->num_q_heads;
+  a.s.NB = desc->num_blocks;
   a.s.B = desc->num_seqs;
   a.s.max_blocks = desc->max_blocks_per_seq;
   a.s.Hkv = desc->num_kv_heads;

@@ -14,6 +14,10 @@
 // Workgroup w handles KV head g = w % Hkv, range k = w / Hkv; consecutive
 // workgroup ids are dealt round-robin to the 8 XCDs, so with Hkv = 8 every
 // XCD streams a single KV head and its L2 keeps that head's shared blocks.
+//
+// Every pointer reaches the kernels as its own __restrict__ parameter: the
+// kernels store only to out / prefix / partials, so the compiler may read
+// block tables through the scalar cache.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,25 +28,24 @@ namespace pa {
 constexpr int kBlock = 16;  // tokens per KV block
 constexpr int kWave = 64;   // lanes per wavefront on gfx950
 
-struct SplitArgs {
-  const int32_t* seq_lens;
-  const int32_t* block_tables;
-  int32_t* prefix;  // [B+1] exclusive prefix of per-sequence block counts
-  float* part_ml;   // [W][2][G][2]  (m in log2 units, l)
-  float* part_o;    // [W][2][G][D]
-  int B;
-  int max_blocks;   // row length of block_tables
-  int Hkv;
-  int G;
-  int Wh;           // ranges (workgroups) per KV head
+// Scalars of one decode launch.
+struct Sched {
+  int B;           // sequences
+  int max_blocks;  // row length of block_tables
+  int Hq;          // query heads
+  int Hkv;         // KV heads
+  int G;           // Hq / Hkv
+  int Wh;          // ranges (workgroups) per KV head
+  int NB;          // physical blocks in the pool
+  float c_log2;    // scale * log2(e) * k_scale: scores in base-2 units
+  float v_scale;   // applied to the output (1 for 16/32-bit pools)
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 // Tokens of sequence b that the kernels attend: clamp to the table row.
-__device__ __forceinline__ int clamped_len(const SplitArgs& a, int b) {
-  int L = a.seq_lens[b];
-  int cap = a.max_blocks * kBlock;
+__device__ __forceinline__ int clamp_len(int L, int max_blocks) {
+  const int cap = max_blocks * kBlock;
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
@@ -69,39 +72,44 @@ __device__ __forceinline__ int readlane(int v, int l) {
   return __builtin_amdgcn_readlane(v, l);
 }
 
-// Total blocks U per head (sum of ceil(len/16)); workgroup 0 also stores the
-// exclusive prefix for the merge kernel.
-__device__ inline int total_blocks(const SplitArgs& a, bool store_prefix) {
+// Total blocks U per head (sum of ceil(len/16)); when `prefix` is non-null
+// the exclusive prefix is stored for the merge kernel.
+__device__ inline int total_blocks(const int32_t* __restrict__ seq_lens,
+                                   int B, int max_blocks,
+                                   int32_t* __restrict__ prefix) {
   const int lane = lane_id();
   int carry = 0;
-  for (int c0 = 0; c0 < a.B; c0 += kWave) {
-    int b = c0 + lane;
-    int nb = b < a.B ? (clamped_len(a, b) + kBlock - 1) / kBlock : 0;
-    int incl = wave_incl_scan(nb) + carry;
-    if (store_prefix && b < a.B) a.prefix[b] = incl - nb;
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const int b = c0 + lane;
+    const int nb =
+        b < B ? (clamp_len(seq_lens[b], max_blocks) + kBlock - 1) / kBlock : 0;
+    const int incl = wave_incl_scan(nb) + carry;
+    if (prefix && b < B) prefix[b] = incl - nb;
     carry = readlane(incl, kWave - 1);
   }
-  if (store_prefix && lane == 0) a.prefix[a.B] = carry;
+  if (prefix && lane == 0) prefix[B] = carry;
   return carry;
 }
 
 // Calls seg(b, Sb, Sb1) for every sequence b (in order) whose block span
 // [Sb, Sb1) overlaps [u0, u1) and is non-empty.  All arguments are uniform.
 template <typename Seg>
-__device__ inline void for_each_segment(const SplitArgs& a, int u0, int u1,
+__device__ inline void for_each_segment(const int32_t* __restrict__ seq_lens,
+                                        int B, int max_blocks, int u0, int u1,
                                         Seg&& seg) {
   const int lane = lane_id();
   int carry = 0;
-  for (int c0 = 0; c0 < a.B; c0 += kWave) {
-    int b = c0 + lane;
-    int nb = b < a.B ? (clamped_len(a, b) + kBlock - 1) / kBlock : 0;
-    int incl = wave_incl_scan(nb) + carry;
-    int excl = incl - nb;
-    int chunk_end = readlane(incl, kWave - 1);
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const int b = c0 + lane;
+    const int nb =
+        b < B ? (clamp_len(seq_lens[b], max_blocks) + kBlock - 1) / kBlock : 0;
+    const int incl = wave_incl_scan(nb) + carry;
+    const int excl = incl - nb;
+    const int chunk_end = readlane(incl, kWave - 1);
     if (chunk_end > u0) {
       uint64_t mask = __ballot(nb > 0 && excl < u1 && incl > u0);
       while (mask) {
-        int i = __builtin_ctzll(mask);
+        const int i = __builtin_ctzll(mask);
         mask &= mask - 1;
         seg(c0 + i, readlane(excl, i), readlane(incl, i));
       }
@@ -117,6 +125,24 @@ __device__ __forceinline__ float fast_exp2(float x) {
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+// max(v[l], v[l ^ 16]) and max(v[l], v[l ^ 32]) with the gfx950 row/half
+// swap instructions (plain VALU, no LDS traffic).  Each swap exchanges one
+// half of the lanes between its two operands; passing the value as both
+// operands puts each lane's partner value in one of the two results.
+__device__ __forceinline__ float max_xor16(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]),
+               __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
+__device__ __forceinline__ float max_xor32(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]),
+               __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
 }  // namespace pa

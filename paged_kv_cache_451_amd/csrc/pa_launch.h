@@ -8,17 +8,18 @@
 
 namespace pa {
 
-// Everything one decode launch needs besides the split schedule.
+// Everything one decode launch needs.
 struct DecodeArgs {
   const void* q;
   const void* k_pool;
   const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
   void* out;
-  float c_log2;   // scale * log2(e) * k_scale: scores in base-2 units
-  float v_scale;  // applied to the output (1 for 16/32-bit pools)
-  int Hq;
-  int NB;
-  SplitArgs s;
+  int32_t* prefix;  // [B+1] exclusive prefix of per-sequence block counts
+  float* part_ml;   // [W][2][G][2]  (m in log2 units, l)
+  float* part_o;    // [W][2][G][D]
+  Sched s;
 };
 
 // Main pass: one 64-lane workgroup per (KV head, block range).
@@ -28,6 +29,9 @@ hipError_t launch_decode_mfma(bool fp8, int head_size, const DecodeArgs& a,
 // Vector-ALU kernel for fp32 q and fp32 KV.
 hipError_t launch_decode_valu(int head_size, const DecodeArgs& a,
                               int num_workgroups, hipStream_t stream);
+// Resident workgroups per compute unit of the main kernels (0 on error).
+int occupancy_decode_mfma(bool fp8, int head_size);
+int occupancy_decode_valu(int head_size);
 
 // Merge pass over sequences whose blocks were split across ranges;
 // grid = B * Hkv workgroups.  out_bf16 selects the output element type.
