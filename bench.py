@@ -23,6 +23,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -45,6 +46,10 @@ def parse():
                    help="pool copies to rotate over (0: enough for >= 2 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the bench, run three plain 1 GiB device "
+                        "copies (the reference kernel that scales HBM "
+                        "byte counters)")
     return p.parse_args()
 
 
@@ -58,17 +63,21 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(config_name: str):
-    """HBM bytes per main-kernel launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"decode_{config_name}_traffic.json")
+    """HBM bytes per main-kernel launch (FETCH_SIZE + WRITE_SIZE, scaled by
+    a plain copy's counts) from the committed rocprofv3 summary of this
+    workload, or None when the summary is missing or was taken on other
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_{config_name}.md")
     try:
         with open(path) as f:
-            rec = json.load(f)
+            text = f.read()
     except OSError:
         return None
+    rec = dict(re.findall(r"^(kernel_source_hash|hbm_bytes_per_launch): "
+                          r"(\S+)$", text, flags=re.M))
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(case, budget_s: float):
@@ -249,6 +258,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_over_algorithmic": (round(traffic / nbytes["decode"], 4)
+                                         if traffic else None),
             "algorithmic_bytes_per_launch": nbytes["decode"],
             "kernel_ms_avg": round(k_avg, 5),
             "kernel_ms_median": round(k_med, 5),
@@ -260,6 +271,14 @@ def main():
     if cfg.lens == "prefix":
         res["roofline"]["achieved_unique"] = round(
             nbytes["decode_unique"] / (k_avg * 1e-3) / 1e9, 2)
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(case, a.cpu_seconds)

@@ -6,8 +6,8 @@
 //     out = sum_i w_i o_i / sum_i w_i l_i.
 // One 64-lane workgroup per (sequence, query head).  The partials' (m, l)
 // pairs are read by all lanes at once (lane i takes partial i) and reduced
-// across the wave; the output rows are then summed with lane l owning
-// columns d = l + 64 r, four partial rows loaded per step.
+// across the wave; the output rows are summed with lane l owning columns
+// d = l + 64 r.
 #include <math.h>
 
 #include "pa_launch.h"
@@ -15,16 +15,14 @@
 namespace pa {
 namespace {
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// Row of partial `k` (a range index) for sequence span starting at block
+// Sb, or -1 when range k is empty and left no partial.
+__device__ __forceinline__ int partial_row(int k, int Sb, int U, int g,
+                                           int n, const Sched& s) {
+  const int r0 = range_begin(k, U, s.Wh);
+  if (r0 == range_begin(k + 1, U, s.Wh)) return -1;
+  const int slot = Sb < r0 ? 0 : 1;
+  return ((g + s.Hkv * k) * 2 + slot) * s.G + n;
 }
 
 template <typename OT, int D>
@@ -32,7 +30,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     OT* __restrict__ out_all, const int32_t* __restrict__ prefix,
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     Sched s) {
-  constexpr int NR = D / 64;
+  constexpr int NR = D / 64;    // output columns per lane
+  constexpr int kRows = 16;     // partial rows loaded per batch
   const int lane = threadIdx.x;
   const int G = s.G;
   const int n = blockIdx.x % G;
@@ -54,64 +53,59 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   if (kf == kl) return;  // finished by the main pass
   const int np = kl - kf + 1;
 
-  // row of partial kf + i, or -1 for an empty range (no partial written)
-  auto row_of = [&](int i) -> int {
-    const int k = kf + i;
-    const int r0 = range_begin(k, U, s.Wh);
-    if (r0 == range_begin(k + 1, U, s.Wh)) return -1;
-    const int slot = Sb < r0 ? 0 : 1;
-    return ((g + s.Hkv * k) * 2 + slot) * G + n;
-  };
-
-  float M = -INFINITY;
-  for (int i0 = 0; i0 < np; i0 += kWave) {
-    const int i = i0 + lane;
-    const int row = i < np ? row_of(i) : -1;
-    const float mi = row >= 0 ? part_ml[(size_t)row * 2] : -INFINITY;
-    M = fmaxf(M, wave_max(mi));
-  }
-  float lsum = 0.f;
+  // Partials are consumed 64 at a time (lane i holds partial i0 + i's m and
+  // l) with a running max across batches; their output rows are read
+  // kRows at a time, the first batch issued before the (m, l) reductions so
+  // that both loads share one memory round trip.
+  float M = -INFINITY, lsum = 0.f;
   float o[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) o[r] = 0.f;
-  if (M != -INFINITY) {
-    for (int i0 = 0; i0 < np; i0 += kWave) {
-      const int i = i0 + lane;
-      const int row = i < np ? row_of(i) : -1;
-      float wi = 0.f;
-      if (row >= 0) {
-        wi = fast_exp2(part_ml[(size_t)row * 2] - M);
-        lsum += wi * part_ml[(size_t)row * 2 + 1];
-      }
-      const int cnt = np - i0 < kWave ? np - i0 : kWave;
-      int t = 0;
-      for (; t + 4 <= cnt; t += 4) {
-        float w4[4], v4[4][NR];
+  for (int i0 = 0; i0 < np; i0 += kWave) {
+    const int cnt = np - i0 < kWave ? np - i0 : kWave;
+    const int row = lane < cnt ? partial_row(kf + i0 + lane, Sb, U, g, n, s)
+                               : -1;
+    float mi = -INFINITY, li = 0.f;
+    if (row >= 0) {
+      mi = part_ml[(size_t)row * 2];
+      li = part_ml[(size_t)row * 2 + 1];
+    }
+    float v[kRows][NR];
+    auto load_rows = [&](int t0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int rr = __builtin_amdgcn_readlane(row, t + u);
-          w4[u] = __builtin_bit_cast(
-              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wi),
-                                               t + u));
-          const float* po = part_o + (size_t)(rr < 0 ? 0 : rr) * D + lane;
-#pragma unroll
-          for (int r = 0; r < NR; ++r) v4[u][r] = rr < 0 ? 0.f : po[64 * r];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int r = 0; r < NR; ++r) o[r] += w4[u] * v4[u][r];
-      }
-      for (; t < cnt; ++t) {
-        const int rr = __builtin_amdgcn_readlane(row, t);
-        const float wt = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wi), t));
+      for (int u = 0; u < kRows; ++u) {
+        const int rr = t0 + u < cnt ? readlane(row, t0 + u) : -1;
         const float* po = part_o + (size_t)(rr < 0 ? 0 : rr) * D + lane;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) o[r] += rr < 0 ? 0.f : wt * po[64 * r];
+        for (int r = 0; r < NR; ++r) v[u][r] = rr < 0 ? 0.f : po[64 * r];
+      }
+    };
+    load_rows(0);
+    float mx = mi;
+#pragma unroll
+    for (int x = 1; x < kWave; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x, kWave));
+    const float m_new = fmaxf(M, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(M - m_use);
+    const float wi = row >= 0 ? fast_exp2(mi - m_use) : 0.f;
+    float wl = wi * li;
+#pragma unroll
+    for (int x = 1; x < kWave; x <<= 1) wl += __shfl_xor(wl, x, kWave);
+    lsum = lsum * alpha + wl;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) o[r] *= alpha;
+    M = m_new;
+    for (int t0 = 0; t0 < cnt; t0 += kRows) {
+      if (t0 > 0) load_rows(t0);
+#pragma unroll
+      for (int u = 0; u < kRows; ++u) {
+        const float w = __builtin_bit_cast(
+            float, readlane(__builtin_bit_cast(int, wi), t0 + u < cnt ? t0 + u
+                                                                       : 0));
+#pragma unroll
+        for (int r = 0; r < NR; ++r) o[r] = fmaf(w, v[u][r], o[r]);
       }
     }
-    lsum = wave_sum(lsum);
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll

@@ -13,7 +13,8 @@
 //   the block's weights broadcast from LDS.
 //
 // Tokens past seq_len (or in blocks with an out-of-range id) get -inf scores
-// and zeroed V values.
+// and zeroed V values.  K/V are read with nontemporal loads (each byte is
+// used once per call).
 #include <math.h>
 
 #include "pa_launch.h"
@@ -86,7 +87,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
       const float* kp = kpool + base + (size_t)t * D + j * DQ;
 #pragma unroll
       for (int i = 0; i < DQ; i += 4) {
-        f32x4 v = *reinterpret_cast<const f32x4*>(kp + i);
+        f32x4 v = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(kp + i));
         kr[i] = v[0]; kr[i + 1] = v[1]; kr[i + 2] = v[2]; kr[i + 3] = v[3];
       }
       float vr[NR][kBlock];
@@ -95,7 +97,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
         const float* vp = vpool + base + (size_t)(lane + 64 * r) * kBlock;
 #pragma unroll
         for (int c = 0; c < kBlock; c += 4) {
-          f32x4 v = *reinterpret_cast<const f32x4*>(vp + c);
+          f32x4 v = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x4*>(vp + c));
 #pragma unroll
           for (int e = 0; e < 4; ++e) vr[r][c + e] = c + e < nv ? v[e] : 0.f;
         }

@@ -1,6 +1,12 @@
 // KV append: each new token's K row goes to its slot's row of the K tile
 // ([16][D] per block and KV head) and its V values to the slot's column of
-// the V tile ([D][16]).  One workgroup per token; a pure byte copy.
+// the V tile ([D][16]).  A pure byte copy.
+//
+// One thread per 16-byte chunk of a token's K row and one per 16-byte chunk
+// of its V row; token i owns workgroups [i * wpt, (i + 1) * wpt).  The chunk
+// loads do not depend on the slot, so a thread issues them together with the
+// slot load and pays one memory round trip before its stores: a K chunk is one 16-byte store, a V chunk
+// becomes 16 / sizeof(T) element stores one V-tile row (16 elements) apart.
 #include "pa_launch.h"
 
 namespace pa {
@@ -9,35 +15,35 @@ namespace {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
-__global__ __launch_bounds__(256) void kv_append_kernel(
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     const T* __restrict__ k_new, const T* __restrict__ v_new,
     const int32_t* __restrict__ slots, T* __restrict__ k_pool,
-    T* __restrict__ v_pool, int hkv, int d, int num_blocks) {
-  const int i = blockIdx.x;
+    T* __restrict__ v_pool, int hkv, int d, int num_blocks, int wpt) {
+  constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  const int i = blockIdx.x / wpt;
+  const int chunks = hkv * d / E;  // chunks of one token's K (or V) row
+  int c = (blockIdx.x - i * wpt) * kAppendThreads + threadIdx.x;
+  const bool is_v = c >= chunks;
+  if (is_v) c -= chunks;
+  if (c >= chunks) return;
+  const size_t row = (size_t)i * hkv * d + (size_t)c * E;
+  const u32x4 val =
+      *reinterpret_cast<const u32x4*>((is_v ? v_new : k_new) + row);
   const int slot = slots[i];
   if (slot < 0 || slot >= num_blocks * kBlock) return;
   const int phys = slot >> 4;
   const int off = slot & (kBlock - 1);
-  const size_t row_elems = (size_t)hkv * d;
-  const T* kn = k_new + (size_t)i * row_elems;
-  const T* vn = v_new + (size_t)i * row_elems;
-  const size_t blk = (size_t)phys * hkv * kBlock * d;
-
-  // K: Hkv rows of D contiguous elements, 16 bytes at a time
-  constexpr int kVec = 16 / (int)sizeof(T);
-  const int vec_per_row = d / kVec;
-  for (int c = threadIdx.x; c < hkv * vec_per_row; c += blockDim.x) {
-    const int g = c / vec_per_row;
-    const int e = (c % vec_per_row) * kVec;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(kn + (size_t)g * d + e);
-    *reinterpret_cast<u32x4*>(k_pool + blk + ((size_t)g * kBlock + off) * d +
-                              e) = v;
-  }
-  // V: one element per (head, d), stride 16 elements in the pool
-  for (int c = threadIdx.x; c < hkv * d; c += blockDim.x) {
-    const int g = c / d;
-    const int e = c % d;
-    v_pool[blk + ((size_t)g * d + e) * kBlock + off] = vn[c];
+  const int g = c * E / d;
+  const int e0 = c * E - g * d;
+  const size_t tile = ((size_t)phys * hkv + g) * kBlock * d;
+  if (!is_v) {
+    *reinterpret_cast<u32x4*>(k_pool + tile + (size_t)off * d + e0) = val;
+  } else {
+    T el[E];
+    __builtin_memcpy(el, &val, sizeof(val));
+    T* vp = v_pool + tile + (size_t)e0 * kBlock + off;
+#pragma unroll
+    for (int e = 0; e < E; ++e) vp[e * kBlock] = el[e];
   }
 }
 
@@ -45,14 +51,22 @@ template <typename T>
 void launch_t(const void* k_new, const void* v_new, const int32_t* slots,
               void* k_pool, void* v_pool, int n, int hkv, int d, int nb,
               hipStream_t stream) {
-  hipLaunchKernelGGL(kv_append_kernel<T>, dim3(n), dim3(256), 0, stream,
+  const int wpt = append_workgroups_per_token((int)sizeof(T), hkv, d);
+  hipLaunchKernelGGL(kv_append_kernel<T>, dim3((unsigned)(n * wpt)),
+                     dim3(kAppendThreads), 0, stream,
                      reinterpret_cast<const T*>(k_new),
                      reinterpret_cast<const T*>(v_new), slots,
                      reinterpret_cast<T*>(k_pool),
-                     reinterpret_cast<T*>(v_pool), hkv, d, nb);
+                     reinterpret_cast<T*>(v_pool), hkv, d, nb, wpt);
 }
 
 }  // namespace
+
+int append_workgroups_per_token(int elem_bytes, int num_kv_heads,
+                                int head_size) {
+  const int chunks = num_kv_heads * head_size * elem_bytes / 16;
+  return (2 * chunks + kAppendThreads - 1) / kAppendThreads;
+}
 
 hipError_t launch_kv_append(int elem_bytes, const void* k_new,
                             const void* v_new, const int32_t* slots,

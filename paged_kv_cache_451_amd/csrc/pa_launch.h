@@ -38,7 +38,11 @@ int occupancy_decode_valu(int head_size);
 hipError_t launch_decode_merge(bool out_bf16, int head_size,
                                const DecodeArgs& a, hipStream_t stream);
 
-// Byte copy of new tokens' K/V rows into pool slots.
+// Byte copy of new tokens' K/V rows into pool slots: num_tokens *
+// append_workgroups_per_token(...) workgroups of kAppendThreads threads.
+constexpr int kAppendThreads = 256;
+int append_workgroups_per_token(int elem_bytes, int num_kv_heads,
+                                int head_size);
 hipError_t launch_kv_append(int elem_bytes, const void* k_new,
                             const void* v_new, const int32_t* slots,
                             void* k_pool, void* v_pool, int num_tokens,
