@@ -102,8 +102,8 @@ __device__ __forceinline__ bf16x8 keep_first(bf16x8 v, int nv) {
 
 // Raw block-table entries of the pair starting at logical block `blk`.  The
 // indices are clamped to the segment's last block hi - 1, so the loads are
-// always in bounds and need no branch; a pair past the segment end reads a
-// block that was just streamed (an L2 hit) and is never computed.
+// always in bounds and need no branch; the second block of a pair that ends
+// the segment repeats the first, so its loads fall on the same lines.
 struct RawIds {
   int e0, e1;
 };
@@ -120,11 +120,12 @@ __device__ __forceinline__ int safe_id(int p, int NB) {
   return (unsigned)p < (unsigned)NB ? p : 0;
 }
 
-// Valid tokens of the two blocks of the pair at `blk` (uniform).
+// Valid tokens of the two blocks of the pair at `blk` (uniform); a pair at
+// or past the segment end `hi` has none.
 __device__ __forceinline__ void pair_valid(const RawIds& r, int blk, int hi,
                                            int L, int NB, int& nv0,
                                            int& nv1) {
-  const bool ok0 = (unsigned)r.e0 < (unsigned)NB;
+  const bool ok0 = blk < hi && (unsigned)r.e0 < (unsigned)NB;
   const bool ok1 = blk + 1 < hi && (unsigned)r.e1 < (unsigned)NB;
   const int a = L - blk * kBlock;
   const int b = a - kBlock;
@@ -240,16 +241,22 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
     const int hi = (Sb1 < u1 ? Sb1 : u1) - Sb;
     const int32_t* trow = block_tables + (size_t)b * sc.max_blocks;
 
-    auto issue = [&](P& pr, const RawIds& id) {
+    // Loads of the pair starting at block pblk.  A pair at or past the end
+    // of the segment is never computed; its loads go to this sequence's q
+    // row (a few lines that are cached anyway) instead of HBM.
+    const T* q_as_t = reinterpret_cast<const T*>(
+        q + ((size_t)b * sc.Hq + (size_t)g * G) * D);
+    auto issue = [&](P& pr, const RawIds& id, int pblk) {
       const size_t base0 = (size_t)safe_id(id.e0, sc.NB) * btile + gtile;
       const size_t base1 = (size_t)safe_id(id.e1, sc.NB) * btile + gtile;
-      pr.load(kpool + (k_hi ? base1 : base0) + k_lane,
-              vpool + (v_hi ? base1 : base0) + v_lane);
+      const bool live = pblk < hi;
+      pr.load(live ? kpool + (k_hi ? base1 : base0) + k_lane : q_as_t,
+              live ? vpool + (v_hi ? base1 : base0) + v_lane : q_as_t);
     };
 
     RawIds ia = raw_ids(trow, lo, hi);
     P A, B;
-    issue(A, ia);
+    issue(A, ia, lo);
     RawIds ib = raw_ids(trow, lo + 2, hi);
 
     // Q as the B operand of QK: lane (n, j) holds head g*G + n.
@@ -324,15 +331,19 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
     };
 
     // Loop invariant: A holds the loads of pair blk, ib the table entries of
-    // pair blk + 2.  Loads are issued unconditionally (see raw_ids).
+    // pair blk + 2.  Loads are issued unconditionally (see raw_ids), and the
+    // loop leaves only after computing both register sets: when a segment
+    // has an odd number of pairs, the last B pair lies past its end and is
+    // computed with every token masked.  A loop exit with one set's loads
+    // still outstanding would make the compiler wait for all loads at the
+    // top of every iteration of the next segment.
     int blk = lo;
     for (;;) {
-      issue(B, ib);
+      issue(B, ib, blk + 2);
       RawIds ic = raw_ids(trow, blk + 4, hi);
       compute(A, ia, blk);
       blk += 2;
-      if (blk >= hi) break;
-      issue(A, ic);
+      issue(A, ic, blk + 2);
       RawIds id = raw_ids(trow, blk + 4, hi);
       compute(B, ib, blk);
       blk += 2;
