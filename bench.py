@@ -46,6 +46,9 @@ def parse():
                    help="pool copies to rotate over (0: enough for >= 2 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--unfused", action="store_true",
+                   help="time the step as three launches (pa_kv_append, "
+                        "then pa_decode) instead of pa_decode_append")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the bench, run three plain 1 GiB device "
                         "copies (the reference kernel that scales HBM "
@@ -180,13 +183,14 @@ def main():
             total_blocks_hint=case.total_blocks, num_waves=a.num_waves,
             events=events)
 
+    fused = not a.unfused
     base_desc = desc_for()
-    ws = _lib.alloc_workspace(base_desc, dev)
+    ws = _lib.alloc_workspace(base_desc, dev, fused=fused)
 
     def prepared(i, desc):
         kp, vp = kps[i % nrot], vps[i % nrot]
         return _lib.PreparedStep(q, kp, vp, tables, lens, case.scale, out,
-                                 desc, ws, k_new, v_new, slots)
+                                 desc, ws, k_new, v_new, slots, fused=fused)
 
     warm = [prepared(i, base_desc) for i in range(a.warmup)]
     timed = [prepared(a.warmup + i, base_desc) for i in range(a.steps)]
@@ -209,7 +213,8 @@ def main():
     # stream, so this runs as its own region after the timed one)
     roof = [_lib.PreparedStep(q, kps[i % nrot], vps[i % nrot], tables, lens,
                               case.scale, out,
-                              desc_for((e0.cuda_event, e1.cuda_event)), ws)
+                              desc_for((e0.cuda_event, e1.cuda_event)), ws,
+                              k_new, v_new, slots, fused=fused)
             for i, (e0, e1) in enumerate(ev)]
     for step in roof:
         step()
@@ -220,7 +225,8 @@ def main():
     k_med = kern_ms[len(kern_ms) // 2]
 
     value = nbytes["step"] / (ms_step * 1e-3) / 1e9
-    achieved = nbytes["decode"] / (k_avg * 1e-3) / 1e9
+    main_bytes = nbytes["main_fused"] if fused else nbytes["decode"]
+    achieved = main_bytes / (k_avg * 1e-3) / 1e9
     traffic = measured_traffic(cfg.name)
     res = {
         "metric": METRIC,
@@ -243,6 +249,8 @@ def main():
             "context_tokens": nbytes["context_tokens"],
             "max_seq_len": case.max_seq_len, "num_blocks": case.num_blocks,
             "seed": seed, "pool_copies_rotated": nrot,
+            "step": ("pa_decode_append (append fused into decode)" if fused
+                     else "pa_kv_append + pa_decode"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(cfg.num_seqs / (ms_step * 1e-3), 1),
@@ -258,9 +266,9 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "traffic_over_algorithmic": (round(traffic / nbytes["decode"], 4)
+            "traffic_over_algorithmic": (round(traffic / main_bytes, 4)
                                          if traffic else None),
-            "algorithmic_bytes_per_launch": nbytes["decode"],
+            "algorithmic_bytes_per_launch": main_bytes,
             "kernel_ms_avg": round(k_avg, 5),
             "kernel_ms_median": round(k_med, 5),
             "kernel_ms_p10": round(kern_ms[len(kern_ms) // 10], 5),

@@ -1,7 +1,8 @@
 /*
  * pa.h - C ABI of the gfx950 paged decode-attention library (libpa.so).
  *
- * Two operations, both from the paged KV-cache design:
+ * Two operations, both from the paged KV-cache design, plus the two fused
+ * into one decode step (pa_decode_append, below):
  *
  *   pa_kv_append  writes each new token's K and V into the pool slot the
  *                 block manager reserved for it.  The block manager takes a
@@ -151,6 +152,53 @@ int pa_decode(const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_tables, const int32_t* seq_lens,
               float scale, void* out, const pa_decode_desc* desc,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace pa_decode_append needs for `desc` on the current
+ * device (0 on an invalid descriptor): that of pa_decode plus one fp32
+ * partial of head_size + 2 values per (sequence, query head).
+ */
+size_t pa_decode_append_workspace_size(const pa_decode_desc* desc);
+
+/*
+ * One decode step in two launches: the append of each sequence's newest
+ * token followed by decode attention that includes it.  The result equals
+ *     pa_kv_append(k_new, v_new, slot_mapping, k_pool, v_pool)  with N = B
+ *     pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out)
+ * (the append step of the block manager: take a block only when the last
+ * one is full, then write the token into the last block - "49 vLLM /
+ * PagedAttention", listing "Таблица блоков"; the attention over the grown
+ * context equals dense attention - "PagedAttention：KV cache 即虚拟内存",
+ * section "直接答案"), up to floating-point rounding order, provided that
+ * slot_mapping[b] is the slot of token seq_lens[b] - 1 of sequence b in
+ * block_tables, in a block no other sequence of the batch reads (the block
+ * manager's allocate-on-growth slot for an unshared last block; writing
+ * into a shared block would need copy-on-write).  A negative slot skips
+ * only the write: the token is still attended from k_new / v_new.
+ *
+ *   q, block_tables, seq_lens, scale, out, desc: as for pa_decode;
+ *     seq_lens[b] counts the new token.
+ *   k_pool, v_pool  written: token b's K row and V column go to
+ *                   slot_mapping[b] (a byte copy; negative or out-of-pool
+ *                   slots are skipped, as in pa_kv_append).
+ *   k_new, v_new    [B][Hkv][D] of kv_dtype, 16-byte aligned: sequence b's
+ *                   newest token (attended from here, not from the pool).
+ *   slot_mapping    int32 [B].
+ *   workspace       at least pa_decode_append_workspace_size(desc) bytes,
+ *                   256-byte aligned.
+ * The main pass attends the first seq_lens[b] - 1 tokens from the pool; the
+ * merge pass writes the new token's K/V, scores it and folds it into the
+ * main pass's partials as one more term of the online softmax.  With
+ * seq_lens[b] <= 0 the row is zero (the slot is still written).
+ * Errors as for pa_decode, plus PA_ERR_NULL for missing k_new / v_new /
+ * slot_mapping and PA_ERR_ALIGN for misaligned ones.
+ */
+int pa_decode_append(const void* q, void* k_pool, void* v_pool,
+                     const int32_t* block_tables, const int32_t* seq_lens,
+                     float scale, void* out, const void* k_new,
+                     const void* v_new, const int32_t* slot_mapping,
+                     const pa_decode_desc* desc, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /*
  * Shapes of one append call.

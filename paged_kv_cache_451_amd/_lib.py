@@ -24,7 +24,8 @@ _DTYPE = {
 }
 
 # names every build of the library exports (checked by the tests)
-EXPORTS = ("pa_decode", "pa_decode_workspace_size", "pa_kv_append",
+EXPORTS = ("pa_decode", "pa_decode_workspace_size", "pa_decode_append",
+           "pa_decode_append_workspace_size", "pa_kv_append",
            "pa_status_string", "pa_abi_version")
 
 
@@ -79,6 +80,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp,
                               ctypes.POINTER(DecodeDesc), vp, sz, vp]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_append_workspace_size.argtypes = [
+        ctypes.POINTER(DecodeDesc)]
+    lib.pa_decode_append_workspace_size.restype = sz
+    lib.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                                     vp, vp, vp, ctypes.POINTER(DecodeDesc),
+                                     vp, sz, vp]
+    lib.pa_decode_append.restype = ctypes.c_int
     lib.pa_kv_append.argtypes = [vp, vp, vp, vp, vp,
                                  ctypes.POINTER(AppendDesc), vp]
     lib.pa_kv_append.restype = ctypes.c_int
@@ -133,12 +141,16 @@ def decode_desc(q: torch.Tensor, k_pool: torch.Tensor,
     return desc
 
 
-def workspace_size(desc: DecodeDesc) -> int:
-    return int(load().pa_decode_workspace_size(ctypes.byref(desc)))
+def workspace_size(desc: DecodeDesc, fused: bool = False) -> int:
+    lib = load()
+    fn = lib.pa_decode_append_workspace_size if fused else \
+        lib.pa_decode_workspace_size
+    return int(fn(ctypes.byref(desc)))
 
 
-def alloc_workspace(desc: DecodeDesc, device=None) -> torch.Tensor:
-    n = max(workspace_size(desc), 256)
+def alloc_workspace(desc: DecodeDesc, device=None,
+                    fused: bool = False) -> torch.Tensor:
+    n = max(workspace_size(desc, fused), 256)
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 
 
@@ -164,6 +176,31 @@ def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *,
     return out
 
 
+def pa_decode_append(q, k_pool, v_pool, block_tables, seq_lens, scale, out,
+                     k_new, v_new, slot_mapping, *, max_seq_len: int,
+                     k_scale: float = 1.0, v_scale: float = 1.0,
+                     total_blocks_hint: int = 0, num_waves: int = 0,
+                     workspace: Optional[torch.Tensor] = None,
+                     events: Optional[Sequence] = None,
+                     desc: Optional[DecodeDesc] = None) -> torch.Tensor:
+    """Append of each sequence's newest token fused with decode attention
+    over the grown context (see ``include/pa.h``)."""
+    lib = load()
+    if desc is None:
+        desc = decode_desc(q, k_pool, block_tables, max_seq_len=max_seq_len,
+                           k_scale=k_scale, v_scale=v_scale,
+                           total_blocks_hint=total_blocks_hint,
+                           num_waves=num_waves, events=events)
+    if workspace is None:
+        workspace = alloc_workspace(desc, q.device, fused=True)
+    _check(lib.pa_decode_append(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        _ptr(seq_lens), ctypes.c_float(scale), _ptr(out), _ptr(k_new),
+        _ptr(v_new), _ptr(slot_mapping), ctypes.byref(desc), _ptr(workspace),
+        workspace.numel(), _stream()))
+    return out
+
+
 def pa_kv_append(k_new, v_new, slot_mapping, k_pool, v_pool) -> None:
     """Write new tokens' K/V into their pool slots (see ``include/pa.h``)."""
     lib = load()
@@ -177,23 +214,36 @@ def pa_kv_append(k_new, v_new, slot_mapping, k_pool, v_pool) -> None:
 
 
 class PreparedStep:
-    """A decode step (append, then decode) with its C arguments marshalled
-    once, for replaying the same call many times (benchmarks, serving loops).
-    Holds references to every tensor it points at."""
+    """A decode step (append, then decode; or both in ``pa_decode_append``
+    when ``fused``) with its C arguments marshalled once, for replaying the
+    same call many times (benchmarks, serving loops).  Holds references to
+    every tensor it points at."""
 
     def __init__(self, q, k_pool, v_pool, block_tables, seq_lens, scale, out,
                  desc: DecodeDesc, workspace: torch.Tensor,
-                 k_new=None, v_new=None, slot_mapping=None):
+                 k_new=None, v_new=None, slot_mapping=None,
+                 fused: bool = False):
         lib = load()
         self._keep = (q, k_pool, v_pool, block_tables, seq_lens, out,
                       workspace, k_new, v_new, slot_mapping, desc)
         stream = _stream()
+        self._append = None
+        if fused:
+            if k_new is None:
+                raise ValueError("the fused step needs k_new/v_new/slots")
+            self._decode = lib.pa_decode_append
+            self._decode_args = (
+                _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
+                _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+                ctypes.byref(desc), _ptr(workspace), workspace.numel(),
+                stream)
+            return
         self._decode = lib.pa_decode
         self._decode_args = (
             _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
             _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
             ctypes.byref(desc), _ptr(workspace), workspace.numel(), stream)
-        self._append = None
         if k_new is not None:
             n, hkv, d = k_new.shape
             self._adesc = AppendDesc(

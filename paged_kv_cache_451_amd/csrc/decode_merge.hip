@@ -25,42 +25,21 @@ __device__ __forceinline__ int partial_row(int k, int Sb, int U, int g,
   return ((g + s.Hkv * k) * 2 + slot) * s.G + n;
 }
 
-template <typename OT, int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(
-    OT* __restrict__ out_all, const int32_t* __restrict__ prefix,
+// Folds the range partials kf..kl of sequence span [Sb, ...) (head n of
+// KV head g) into the running (M, lsum, o).  Partials are consumed 64 at a
+// time (lane i holds partial i0 + i's m and l) with a running max across
+// batches; their output rows are read kRows at a time, the first batch
+// issued before the (m, l) reductions so that both loads share one memory
+// round trip.
+template <int D>
+__device__ inline void fold_range_partials(
+    int kf, int kl, int Sb, int U, int g, int n, const Sched& s,
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
-    Sched s) {
-  constexpr int NR = D / 64;    // output columns per lane
-  constexpr int kRows = 16;     // partial rows loaded per batch
+    float& M, float& lsum, float (&o)[D / 64]) {
+  constexpr int NR = D / 64;
+  constexpr int kRows = 16;
   const int lane = threadIdx.x;
-  const int G = s.G;
-  const int n = blockIdx.x % G;
-  const int bg = blockIdx.x / G;
-  const int b = bg / s.Hkv;
-  const int g = bg % s.Hkv;
-  const int Sb = prefix[b];
-  const int Sb1 = prefix[b + 1];
-  const int U = prefix[s.B];
-  OT* out = out_all + ((size_t)b * s.Hq + (size_t)g * G + n) * D;
-
-  if (Sb1 == Sb) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) out[lane + 64 * r] = (OT)0.f;
-    return;
-  }
-  const int kf = range_of(Sb, U, s.Wh);
-  const int kl = range_of(Sb1 - 1, U, s.Wh);
-  if (kf == kl) return;  // finished by the main pass
   const int np = kl - kf + 1;
-
-  // Partials are consumed 64 at a time (lane i holds partial i0 + i's m and
-  // l) with a running max across batches; their output rows are read
-  // kRows at a time, the first batch issued before the (m, l) reductions so
-  // that both loads share one memory round trip.
-  float M = -INFINITY, lsum = 0.f;
-  float o[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) o[r] = 0.f;
   for (int i0 = 0; i0 < np; i0 += kWave) {
     const int cnt = np - i0 < kWave ? np - i0 : kWave;
     const int row = lane < cnt ? partial_row(kf + i0 + lane, Sb, U, g, n, s)
@@ -107,7 +86,173 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
       }
     }
   }
+}
+
+template <typename OT, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(
+    OT* __restrict__ out_all, const int32_t* __restrict__ prefix,
+    const float* __restrict__ part_ml, const float* __restrict__ part_o,
+    Sched s) {
+  constexpr int NR = D / 64;  // output columns per lane
+  const int lane = threadIdx.x;
+  const int G = s.G;
+  const int n = blockIdx.x % G;
+  const int bg = blockIdx.x / G;
+  const int b = bg / s.Hkv;
+  const int g = bg % s.Hkv;
+  const int Sb = prefix[b];
+  const int Sb1 = prefix[b + 1];
+  const int U = prefix[s.B];
+  OT* out = out_all + ((size_t)b * s.Hq + (size_t)g * G + n) * D;
+
+  if (Sb1 == Sb) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) out[lane + 64 * r] = (OT)0.f;
+    return;
+  }
+  const int kf = range_of(Sb, U, s.Wh);
+  const int kl = range_of(Sb1 - 1, U, s.Wh);
+  if (kf == kl) return;  // finished by the main pass
+
+  float M = -INFINITY, lsum = 0.f;
+  float o[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) o[r] = 0.f;
+  fold_range_partials<D>(kf, kl, Sb, U, g, n, s, part_ml, part_o, M, lsum,
+                         o);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) out[lane + 64 * r] = (OT)(o[r] * inv);
+}
+
+// Storage element of a K/V pool: raw bits for the byte copy, and the value.
+template <int KB>
+struct KvElem;
+template <>
+struct KvElem<4> {
+  typedef uint32_t raw;
+  typedef float io;  // q and out element type paired with this pool
+  __device__ static float value(raw r) { return __builtin_bit_cast(float, r); }
+};
+template <>
+struct KvElem<2> {
+  typedef uint16_t raw;
+  typedef __bf16 io;
+  __device__ static float value(raw r) {
+    return __builtin_bit_cast(float, (uint32_t)r << 16);
+  }
+};
+template <>
+struct KvElem<1> {
+  typedef uint8_t raw;
+  typedef __bf16 io;
+  __device__ static float value(raw r) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)r, 0);
+  }
+};
+
+// Merge pass of the fused append + decode step, one 64-lane workgroup per
+// (sequence, query head).  The main pass attended to every cached token but
+// the newest one (len_bias = 1) and left partials: range partials for
+// sequences split between ranges, a direct partial for a sequence one range
+// finished.  This pass
+//   * writes the newest token's K row and V column for KV head g into its
+//     slot (the workgroup of the group's first query head; a byte copy),
+//   * scores that token from k_new (s = scale * log2e * k_scale * <q, k>),
+//   * and folds it into the sequence's partials as one more term of the
+//     online softmax:  out = (sum_i w_i o_i + 2^(s-M) v_scale v_new) /
+//                            (sum_i w_i l_i + 2^(s-M)).
+// The pool slot is not read by this call's main pass (its position is at or
+// past the attended length), so the write needs no ordering with it.
+template <int KB, int D>
+__global__ __launch_bounds__(64) void decode_merge_append_kernel(
+    typename KvElem<KB>::io* __restrict__ out_all,
+    const typename KvElem<KB>::io* __restrict__ q,
+    const int32_t* __restrict__ prefix, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ slots,
+    const typename KvElem<KB>::raw* __restrict__ k_new,
+    const typename KvElem<KB>::raw* __restrict__ v_new,
+    typename KvElem<KB>::raw* __restrict__ k_pool,
+    typename KvElem<KB>::raw* __restrict__ v_pool,
+    const float* __restrict__ part_ml, const float* __restrict__ part_o,
+    const float* __restrict__ direct_ml, const float* __restrict__ direct_o,
+    Sched s) {
+  typedef KvElem<KB> E;
+  typedef typename E::io OT;
+  typedef typename E::raw RT;
+  constexpr int NR = D / 64;
+  const int lane = threadIdx.x;
+  const int G = s.G;
+  const int n = blockIdx.x % G;
+  const int bg = blockIdx.x / G;
+  const int b = bg / s.Hkv;
+  const int g = bg % s.Hkv;
+  const size_t h_row = (size_t)b * s.Hq + (size_t)g * G + n;
+  const size_t kv_row = ((size_t)b * s.Hkv + g) * D;
+
+  // independent loads: one memory round trip
+  const int Sb = prefix[b];
+  const int Sb1 = prefix[b + 1];
+  const int U = prefix[s.B];
+  const int L = seq_lens[b];
+  const int slot = slots[b];
+  RT kr[NR], vr[NR];
+  float qf[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int d = lane + 64 * r;
+    kr[r] = k_new[kv_row + d];
+    vr[r] = v_new[kv_row + d];
+    qf[r] = (float)q[h_row * D + d];
+  }
+
+  if (n == 0 && slot >= 0 && slot < s.NB * kBlock) {
+    const size_t tile = ((size_t)(slot >> 4) * s.Hkv + g) * kBlock * D;
+    const int off = slot & (kBlock - 1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int d = lane + 64 * r;
+      k_pool[tile + (size_t)off * D + d] = kr[r];
+      v_pool[tile + (size_t)d * kBlock + off] = vr[r];
+    }
+  }
+
+  float dot = 0.f;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) dot = fmaf(qf[r], E::value(kr[r]), dot);
+#pragma unroll
+  for (int x = 1; x < kWave; x <<= 1) dot += __shfl_xor(dot, x, kWave);
+
+  float M = -INFINITY, lsum = 0.f;
+  float o[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) o[r] = 0.f;
+  if (Sb1 > Sb) {
+    const int kf = range_of(Sb, U, s.Wh);
+    const int kl = range_of(Sb1 - 1, U, s.Wh);
+    if (kf == kl) {
+      M = direct_ml[h_row * 2];
+      lsum = direct_ml[h_row * 2 + 1];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) o[r] = direct_o[h_row * D + lane + 64 * r];
+    } else {
+      fold_range_partials<D>(kf, kl, Sb, U, g, n, s, part_ml, part_o, M,
+                             lsum, o);
+    }
+  }
+  if (L >= 1) {  // the newest token, from k_new / v_new
+    const float sn = dot * s.c_log2;
+    const float m_new = fmaxf(M, sn);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(M - m_use);
+    const float w = fast_exp2(sn - m_use);
+    lsum = lsum * alpha + w;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      o[r] = fmaf(w * s.v_scale, E::value(vr[r]), o[r] * alpha);
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  OT* out = out_all + h_row * D;
 #pragma unroll
   for (int r = 0; r < NR; ++r) out[lane + 64 * r] = (OT)(o[r] * inv);
 }
@@ -131,7 +276,46 @@ hipError_t launch_m(int head_size, const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int KB, int D>
+void launch_append_one(const DecodeArgs& a, hipStream_t stream) {
+  typedef KvElem<KB> E;
+  const dim3 grid((unsigned)(a.s.B * a.s.Hq));
+  hipLaunchKernelGGL(
+      (decode_merge_append_kernel<KB, D>), grid, dim3(64), 0, stream,
+      reinterpret_cast<typename E::io*>(a.out),
+      reinterpret_cast<const typename E::io*>(a.q), a.prefix, a.seq_lens,
+      a.slots, reinterpret_cast<const typename E::raw*>(a.k_new),
+      reinterpret_cast<const typename E::raw*>(a.v_new),
+      reinterpret_cast<typename E::raw*>(a.k_pool_w),
+      reinterpret_cast<typename E::raw*>(a.v_pool_w), a.part_ml, a.part_o,
+      a.direct_ml, a.direct_o, a.s);
+}
+
+template <int KB>
+hipError_t launch_append_d(int head_size, const DecodeArgs& a,
+                           hipStream_t stream) {
+  switch (head_size) {
+    case 64: launch_append_one<KB, 64>(a, stream); break;
+    case 128: launch_append_one<KB, 128>(a, stream); break;
+    case 256: launch_append_one<KB, 256>(a, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_decode_merge_append(int kv_bytes, int head_size,
+                                      const DecodeArgs& a,
+                                      hipStream_t stream) {
+  if (a.s.B == 0) return hipSuccess;
+  switch (kv_bytes) {
+    case 4: return launch_append_d<4>(head_size, a, stream);
+    case 2: return launch_append_d<2>(head_size, a, stream);
+    case 1: return launch_append_d<1>(head_size, a, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode_merge(bool out_bf16, int head_size,
                                const DecodeArgs& a, hipStream_t stream) {

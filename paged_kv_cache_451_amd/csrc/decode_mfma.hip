@@ -203,7 +203,8 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
     const void* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, __bf16* __restrict__ out,
     int32_t* __restrict__ prefix, float* __restrict__ part_ml,
-    float* __restrict__ part_o, Sched sc) {
+    float* __restrict__ part_o, float* __restrict__ direct_ml,
+    float* __restrict__ direct_o, Sched sc) {
   typedef Pair<FP8, D> P;
   typedef typename P::T T;
   constexpr int NC = P::NC;
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
   const int k = w / sc.Hkv;
   const int G = sc.G;
 
-  const int U = total_blocks(seq_lens, sc.B, sc.max_blocks,
+  const int U = total_blocks(seq_lens, sc.B, sc.max_blocks, sc.len_bias,
                              w == 0 ? prefix : nullptr);
   const int u0 = range_begin(k, U, sc.Wh);
   const int u1 = range_begin(k + 1, U, sc.Wh);
@@ -234,9 +235,9 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
   const bool k_hi = r16 >= 8;  // K row from the pair's second block
   const bool v_hi = j >= 2;    // V tokens from the pair's second block
 
-  for_each_segment(seq_lens, sc.B, sc.max_blocks, u0, u1,
+  for_each_segment(seq_lens, sc.B, sc.max_blocks, sc.len_bias, u0, u1,
                    [&](int b, int Sb, int Sb1) {
-    const int L = clamp_len(seq_lens[b], sc.max_blocks);
+    const int L = pool_len(seq_lens[b], sc.len_bias, sc.max_blocks);
     const int lo = (Sb > u0 ? Sb : u0) - Sb;
     const int hi = (Sb1 < u1 ? Sb1 : u1) - Sb;
     const int32_t* trow = block_tables + (size_t)b * sc.max_blocks;
@@ -358,7 +359,18 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
     const int n = r16;
     if (n < G) {
       const bool split = Sb < u0 || Sb1 > u1;
-      if (!split) {
+      if (!split && sc.len_bias) {
+        // the merge pass still has to fold in the appended token
+        const size_t row = (size_t)b * sc.Hq + (size_t)g * G + n;
+        float* po = direct_o + row * D + 4 * j;
+#pragma unroll
+        for (int xx = 0; xx < NX; ++xx)
+          *reinterpret_cast<f32x4*>(po + 16 * xx) = acc[xx] * sc.v_scale;
+        if (j == 0) {
+          direct_ml[row * 2 + 0] = m;
+          direct_ml[row * 2 + 1] = ltot;
+        }
+      } else if (!split) {
         const float inv = ltot > 0.f ? sc.v_scale / ltot : 0.f;
         __bf16* orow = out + ((size_t)b * sc.Hq + (size_t)g * G + n) * D +
                        4 * j;
@@ -391,7 +403,7 @@ void launch_one(const DecodeArgs& a, int nwg, hipStream_t stream) {
                      stream, reinterpret_cast<const __bf16*>(a.q), a.k_pool,
                      a.v_pool, a.block_tables, a.seq_lens,
                      reinterpret_cast<__bf16*>(a.out), a.prefix, a.part_ml,
-                     a.part_o, a.s);
+                     a.part_o, a.direct_ml, a.direct_o, a.s);
 }
 
 template <bool FP8, int D>

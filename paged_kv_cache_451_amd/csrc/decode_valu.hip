@@ -32,7 +32,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
     const float* __restrict__ vpool, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, float* __restrict__ out,
     int32_t* __restrict__ prefix, float* __restrict__ part_ml,
-    float* __restrict__ part_o, Sched sc) {
+    float* __restrict__ part_o, float* __restrict__ direct_ml,
+    float* __restrict__ direct_o, Sched sc) {
   constexpr int DQ = D / 4;   // K values per lane (a quarter row)
   constexpr int NR = D / 64;  // output columns per lane
   __shared__ float qs[kMaxG][D];
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
   const int k = w / sc.Hkv;
   const int G = sc.G;
 
-  const int U = total_blocks(seq_lens, sc.B, sc.max_blocks,
+  const int U = total_blocks(seq_lens, sc.B, sc.max_blocks, sc.len_bias,
                              w == 0 ? prefix : nullptr);
   const int u0 = range_begin(k, U, sc.Wh);
   const int u1 = range_begin(k + 1, U, sc.Wh);
@@ -54,9 +55,9 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
 
   const size_t tile = (size_t)kBlock * D;
 
-  for_each_segment(seq_lens, sc.B, sc.max_blocks, u0, u1,
+  for_each_segment(seq_lens, sc.B, sc.max_blocks, sc.len_bias, u0, u1,
                    [&](int b, int Sb, int Sb1) {
-    const int L = clamp_len(seq_lens[b], sc.max_blocks);
+    const int L = pool_len(seq_lens[b], sc.len_bias, sc.max_blocks);
     const int lo = (Sb > u0 ? Sb : u0) - Sb;
     const int hi = (Sb1 < u1 ? Sb1 : u1) - Sb;
     const int32_t* trow = block_tables + (size_t)b * sc.max_blocks;
@@ -148,7 +149,17 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
 #pragma unroll
     for (int n = 0; n < kMaxG; ++n) {
       if (n >= G) break;
-      if (!split) {
+      if (!split && sc.len_bias) {
+        // the merge pass still has to fold in the appended token
+        const size_t row = (size_t)b * sc.Hq + (size_t)g * G + n;
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+          direct_o[row * D + lane + 64 * r] = o[n][r] * sc.v_scale;
+        if (lane == 0) {
+          direct_ml[row * 2 + 0] = m[n];
+          direct_ml[row * 2 + 1] = l[n];
+        }
+      } else if (!split) {
         const float inv = l[n] > 0.f ? sc.v_scale / l[n] : 0.f;
         float* orow = out + ((size_t)b * sc.Hq + (size_t)g * G + n) * D;
 #pragma unroll
@@ -175,7 +186,7 @@ void launch_one(const DecodeArgs& a, int nwg, hipStream_t stream) {
                      reinterpret_cast<const float*>(a.k_pool),
                      reinterpret_cast<const float*>(a.v_pool), a.block_tables,
                      a.seq_lens, reinterpret_cast<float*>(a.out), a.prefix,
-                     a.part_ml, a.part_o, a.s);
+                     a.part_ml, a.part_o, a.direct_ml, a.direct_o, a.s);
 }
 
 template <int D>

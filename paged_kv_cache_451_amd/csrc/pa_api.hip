@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 // Upper bound on 64-lane workgroups per compute unit the schedule aims for;
 // the kernel's register budget may allow fewer.  Measured on MI355X: four
 // per CU streams as fast as eight or more while giving each range twice the
@@ -88,13 +88,13 @@ int check_desc(const pa_decode_desc* d) {
 struct Plan {
   int Wh;  // ranges per KV head
   int W;   // workgroups of the main pass
-  size_t off_ml, off_o, bytes;
+  size_t off_ml, off_o, off_dml, off_do, bytes;
 };
 
 // Ranges per KV head: enough resident workgroups to fill every CU, but no
 // range shorter than kMinBlocksPerRange blocks when the total is known or
 // bounded.
-bool make_plan(const pa_decode_desc* d, Plan* p) {
+bool make_plan(const pa_decode_desc* d, bool fused, Plan* p) {
   const int hkv = d->num_kv_heads;
   const int G = d->num_q_heads / hkv;
   int64_t wh;
@@ -128,7 +128,91 @@ bool make_plan(const pa_decode_desc* d, Plan* p) {
   p->off_ml = prefix;
   p->off_o = p->off_ml + round_up(rows * 2 * sizeof(float));
   p->bytes = p->off_o + round_up(rows * d->head_size * sizeof(float));
+  p->off_dml = p->off_do = 0;
+  if (fused) {  // direct partials, one per (sequence, query head)
+    const size_t hrows = (size_t)d->num_seqs * d->num_q_heads;
+    p->off_dml = p->bytes;
+    p->off_do = p->off_dml + round_up(hrows * 2 * sizeof(float));
+    p->bytes = p->off_do + round_up(hrows * d->head_size * sizeof(float));
+  }
   return true;
+}
+
+// Both decode entry points; k_new == nullptr selects the plain decode.
+int run_decode(const void* q, const void* k_pool, const void* v_pool,
+               const int32_t* block_tables, const int32_t* seq_lens,
+               float scale, void* out, const void* k_new, const void* v_new,
+               const int32_t* slots, void* k_pool_w, void* v_pool_w,
+               const pa_decode_desc* desc, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != PA_OK) return st;
+  const bool fused = k_new != nullptr;
+  if (desc->num_seqs == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out)
+    return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned16(out) || ((uintptr_t)block_tables & 3u) ||
+      ((uintptr_t)seq_lens & 3u))
+    return PA_ERR_ALIGN;
+  if (fused && (!aligned16(k_new) || !aligned16(v_new) ||
+                ((uintptr_t)slots & 3u)))
+    return PA_ERR_ALIGN;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  Plan p;
+  if (!make_plan(desc, fused, &p)) return PA_ERR_DEVICE;
+  if (!workspace || workspace_bytes < p.bytes) return PA_ERR_WORKSPACE;
+  if ((uintptr_t)workspace % kAlign) return PA_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  pa::DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.prefix = reinterpret_cast<int32_t*>(ws);
+  a.part_ml = reinterpret_cast<float*>(ws + p.off_ml);
+  a.part_o = reinterpret_cast<float*>(ws + p.off_o);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slots = slots;
+  a.k_pool_w = k_pool_w;
+  a.v_pool_w = v_pool_w;
+  a.direct_ml = fused ? reinterpret_cast<float*>(ws + p.off_dml) : nullptr;
+  a.direct_o = fused ? reinterpret_cast<float*>(ws + p.off_do) : nullptr;
+  const float k_scale = desc->kv_dtype == PA_FP8_E4M3FN ? desc->k_scale : 1.f;
+  a.s.c_log2 = (float)((double)scale * 1.4426950408889634 * (double)k_scale);
+  a.s.v_scale = desc->kv_dtype == PA_FP8_E4M3FN ? desc->v_scale : 1.f;
+  a.s.Hq = desc->num_q_heads;
+  a.s.NB = desc->num_blocks;
+  a.s.B = desc->num_seqs;
+  a.s.max_blocks = desc->max_blocks_per_seq;
+  a.s.Hkv = desc->num_kv_heads;
+  a.s.G = desc->num_q_heads / desc->num_kv_heads;
+  a.s.Wh = p.Wh;
+  a.s.len_bias = fused ? 1 : 0;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(
+      const_cast<void**>(desc->profile_events));
+  if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return PA_ERR_LAUNCH;
+  hipError_t e;
+  if (desc->kv_dtype == PA_F32)
+    e = pa::launch_decode_valu(desc->head_size, a, p.W, s);
+  else
+    e = pa::launch_decode_mfma(desc->kv_dtype == PA_FP8_E4M3FN,
+                               desc->head_size, a, p.W, s);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return PA_ERR_LAUNCH;
+  if (fused)
+    e = pa::launch_decode_merge_append((int)dtype_bytes(desc->kv_dtype),
+                                       desc->head_size, a, s);
+  else
+    e = pa::launch_decode_merge(desc->q_dtype == PA_BF16, desc->head_size, a,
+                                s);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -155,7 +239,15 @@ size_t pa_decode_workspace_size(const pa_decode_desc* desc) {
   if (check_desc(desc) != PA_OK) return 0;
   if (desc->num_seqs == 0) return 0;
   Plan p;
-  if (!make_plan(desc, &p)) return 0;
+  if (!make_plan(desc, false, &p)) return 0;
+  return p.bytes;
+}
+
+size_t pa_decode_append_workspace_size(const pa_decode_desc* desc) {
+  if (check_desc(desc) != PA_OK) return 0;
+  if (desc->num_seqs == 0) return 0;
+  Plan p;
+  if (!make_plan(desc, true, &p)) return 0;
   return p.bytes;
 }
 
@@ -163,58 +255,24 @@ int pa_decode(const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_tables, const int32_t* seq_lens,
               float scale, void* out, const pa_decode_desc* desc,
               void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_desc(desc);
-  if (st != PA_OK) return st;
-  if (desc->num_seqs == 0) return PA_OK;
-  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out)
+  return run_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out,
+                    nullptr, nullptr, nullptr, nullptr, nullptr, desc,
+                    workspace, workspace_bytes, stream);
+}
+
+int pa_decode_append(const void* q, void* k_pool, void* v_pool,
+                     const int32_t* block_tables, const int32_t* seq_lens,
+                     float scale, void* out, const void* k_new,
+                     const void* v_new, const int32_t* slot_mapping,
+                     const pa_decode_desc* desc, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!desc) return PA_ERR_NULL;
+  if (desc->num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
     return PA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
-      !aligned16(out) || ((uintptr_t)block_tables & 3u) ||
-      ((uintptr_t)seq_lens & 3u))
-    return PA_ERR_ALIGN;
-  if (!isfinite(scale)) return PA_ERR_SHAPE;
-  Plan p;
-  if (!make_plan(desc, &p)) return PA_ERR_DEVICE;
-  if (!workspace || workspace_bytes < p.bytes) return PA_ERR_WORKSPACE;
-  if ((uintptr_t)workspace % kAlign) return PA_ERR_ALIGN;
-
-  char* ws = static_cast<char*>(workspace);
-  pa::DecodeArgs a;
-  a.q = q;
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
-  a.block_tables = block_tables;
-  a.seq_lens = seq_lens;
-  a.out = out;
-  a.prefix = reinterpret_cast<int32_t*>(ws);
-  a.part_ml = reinterpret_cast<float*>(ws + p.off_ml);
-  a.part_o = reinterpret_cast<float*>(ws + p.off_o);
-  const float k_scale = desc->kv_dtype == PA_FP8_E4M3FN ? desc->k_scale : 1.f;
-  a.s.c_log2 = (float)((double)scale * 1.4426950408889634 * (double)k_scale);
-  a.s.v_scale = desc->kv_dtype == PA_FP8_E4M3FN ? desc->v_scale : 1.f;
-  a.s.Hq = desc->num_q_heads;
-  a.s.NB = desc->num_blocks;
-  a.s.B = desc->num_seqs;
-  a.s.max_blocks = desc->max_blocks_per_seq;
-  a.s.Hkv = desc->num_kv_heads;
-  a.s.G = desc->num_q_heads / desc->num_kv_heads;
-  a.s.Wh = p.Wh;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(
-      const_cast<void**>(desc->profile_events));
-  if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return PA_ERR_LAUNCH;
-  hipError_t e;
-  if (desc->kv_dtype == PA_F32)
-    e = pa::launch_decode_valu(desc->head_size, a, p.W, s);
-  else
-    e = pa::launch_decode_mfma(desc->kv_dtype == PA_FP8_E4M3FN,
-                               desc->head_size, a, p.W, s);
-  if (e != hipSuccess) return PA_ERR_LAUNCH;
-  if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return PA_ERR_LAUNCH;
-  e = pa::launch_decode_merge(desc->q_dtype == PA_BF16, desc->head_size, a,
-                              s);
-  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  if (desc->num_seqs == 0) return check_desc(desc);
+  return run_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out,
+                    k_new, v_new, slot_mapping, k_pool, v_pool, desc,
+                    workspace, workspace_bytes, stream);
 }
 
 int pa_kv_append(const void* k_new, const void* v_new,

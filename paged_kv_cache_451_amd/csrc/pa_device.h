@@ -39,13 +39,18 @@ struct Sched {
   int NB;          // physical blocks in the pool
   float c_log2;    // scale * log2(e) * k_scale: scores in base-2 units
   float v_scale;   // applied to the output (1 for 16/32-bit pools)
+  int len_bias;    // newest tokens per sequence that are not read from the
+                   // pool (1 when the step's appended token is folded in by
+                   // the merge pass, else 0)
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Tokens of sequence b that the kernels attend: clamp to the table row.
-__device__ __forceinline__ int clamp_len(int L, int max_blocks) {
+// Tokens of a sequence of length L that are read from the pool: L minus the
+// tokens supplied separately, clamped to the table row.
+__device__ __forceinline__ int pool_len(int L, int bias, int max_blocks) {
   const int cap = max_blocks * kBlock;
+  L -= bias;
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
@@ -75,14 +80,15 @@ __device__ __forceinline__ int readlane(int v, int l) {
 // Total blocks U per head (sum of ceil(len/16)); when `prefix` is non-null
 // the exclusive prefix is stored for the merge kernel.
 __device__ inline int total_blocks(const int32_t* __restrict__ seq_lens,
-                                   int B, int max_blocks,
+                                   int B, int max_blocks, int bias,
                                    int32_t* __restrict__ prefix) {
   const int lane = lane_id();
   int carry = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int b = c0 + lane;
     const int nb =
-        b < B ? (clamp_len(seq_lens[b], max_blocks) + kBlock - 1) / kBlock : 0;
+        b < B ? (pool_len(seq_lens[b], bias, max_blocks) + kBlock - 1) / kBlock
+              : 0;
     const int incl = wave_incl_scan(nb) + carry;
     if (prefix && b < B) prefix[b] = incl - nb;
     carry = readlane(incl, kWave - 1);
@@ -95,14 +101,15 @@ __device__ inline int total_blocks(const int32_t* __restrict__ seq_lens,
 // [Sb, Sb1) overlaps [u0, u1) and is non-empty.  All arguments are uniform.
 template <typename Seg>
 __device__ inline void for_each_segment(const int32_t* __restrict__ seq_lens,
-                                        int B, int max_blocks, int u0, int u1,
-                                        Seg&& seg) {
+                                        int B, int max_blocks, int bias,
+                                        int u0, int u1, Seg&& seg) {
   const int lane = lane_id();
   int carry = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int b = c0 + lane;
     const int nb =
-        b < B ? (clamp_len(seq_lens[b], max_blocks) + kBlock - 1) / kBlock : 0;
+        b < B ? (pool_len(seq_lens[b], bias, max_blocks) + kBlock - 1) / kBlock
+              : 0;
     const int incl = wave_incl_scan(nb) + carry;
     const int excl = incl - nb;
     const int chunk_end = readlane(incl, kWave - 1);

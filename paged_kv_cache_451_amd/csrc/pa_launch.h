@@ -19,6 +19,15 @@ struct DecodeArgs {
   int32_t* prefix;  // [B+1] exclusive prefix of per-sequence block counts
   float* part_ml;   // [W][2][G][2]  (m in log2 units, l)
   float* part_o;    // [W][2][G][D]
+  // Fused append (s.len_bias = 1): the step's new token per sequence, its
+  // pool slot, and the partials of sequences one range finished entirely.
+  const void* k_new;       // [B][Hkv][D] pool element type
+  const void* v_new;       // [B][Hkv][D]
+  const int32_t* slots;    // [B]
+  void* k_pool_w;          // the pools again, written by the merge pass
+  void* v_pool_w;
+  float* direct_ml;        // [B][Hq][2]
+  float* direct_o;         // [B][Hq][D]
   Sched s;
 };
 
@@ -34,9 +43,15 @@ int occupancy_decode_mfma(bool fp8, int head_size);
 int occupancy_decode_valu(int head_size);
 
 // Merge pass over sequences whose blocks were split across ranges;
-// grid = B * Hkv workgroups.  out_bf16 selects the output element type.
+// grid = B * Hq workgroups.  out_bf16 selects the output element type.
 hipError_t launch_decode_merge(bool out_bf16, int head_size,
                                const DecodeArgs& a, hipStream_t stream);
+// Merge pass of the fused step: every (sequence, query head) combines its
+// partials with the appended token, and the token's K/V go to their slot.
+// kv_bytes: element size of the pools (4 = f32, 2 = bf16, 1 = fp8 e4m3fn).
+hipError_t launch_decode_merge_append(int kv_bytes, int head_size,
+                                      const DecodeArgs& a,
+                                      hipStream_t stream);
 
 // Byte copy of new tokens' K/V rows into pool slots: num_tokens *
 // append_workgroups_per_token(...) workgroups of kAppendThreads threads.

@@ -325,7 +325,16 @@ def algorithmic_bytes(case: DecodeCase) -> dict:
             uniq_tokens += tok
     kv_unique = uniq_tokens * hkv * d * 2 * s_kv
     decode = kv + qo + tables + scales
+    # the main pass of the fused step streams every cached token but the
+    # newest (which the merge pass takes from k_new / v_new), reads q, the
+    # table entries of those tokens and the lengths
+    prev = (lens - 1).clamp(min=0)
+    main_fused = (int(prev.sum()) * hkv * d * 2 * s_kv
+                  + b * cfg.num_q_heads * d * s_q
+                  + int(((prev + BLOCK_SIZE - 1) // BLOCK_SIZE).sum()) * 4
+                  + b * 4 + scales)
     return {"kv": kv, "kv_unique": kv_unique, "decode": decode,
             "decode_unique": kv_unique + qo + tables + scales,
+            "main_fused": main_fused,
             "append": append, "step": decode + append,
             "context_tokens": int(lens.sum())}

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
     assert lib.pa_status_string(0) == b"success"
     for st in range(-7, 0):
         assert lib.pa_status_string(st) not in (b"", b"unknown status")
@@ -99,10 +99,35 @@ def _desc(**kw):
 def test_invalid_descriptors_are_rejected_before_any_launch(lib, bad, status):
     d = _desc(**bad)
     assert lib.pa_decode_workspace_size(ctypes.byref(d)) == 0
+    assert lib.pa_decode_append_workspace_size(ctypes.byref(d)) == 0
     dummy = ctypes.c_void_p(16)
     rc = lib.pa_decode(dummy, dummy, dummy, dummy, dummy, ctypes.c_float(1.0),
                        dummy, ctypes.byref(d), dummy, 1 << 20, None)
     assert rc == status
+    rc = lib.pa_decode_append(dummy, dummy, dummy, dummy, dummy,
+                              ctypes.c_float(1.0), dummy, dummy, dummy, dummy,
+                              ctypes.byref(d), dummy, 1 << 20, None)
+    assert rc == status
+
+
+def test_fused_step_checks_its_extra_pointers(lib):
+    d = _desc()
+    p, odd = ctypes.c_void_p(256), ctypes.c_void_p(258)
+    args = [p] * 5 + [ctypes.c_float(1.0), p]
+    assert lib.pa_decode_append(*args, None, p, p, ctypes.byref(d), p,
+                                1 << 20, None) == -1
+    assert lib.pa_decode_append(*args, p, p, None, ctypes.byref(d), p,
+                                1 << 20, None) == -1
+    assert lib.pa_decode_append(*args, odd, p, p, ctypes.byref(d), p,
+                                1 << 20, None) == -4
+    assert lib.pa_decode_append(*args, p, p, ctypes.c_void_p(258),
+                                ctypes.byref(d), p, 1 << 20, None) == -4
+    assert lib.pa_decode_append(*args, p, p, p, None, p, 1 << 20,
+                                None) == -1
+    e = _desc(num_seqs=0)
+    assert lib.pa_decode_append(None, None, None, None, None,
+                                ctypes.c_float(1.0), None, None, None, None,
+                                ctypes.byref(e), None, 0, None) == 0
 
 
 def test_null_pointers_and_alignment_are_rejected(lib):
