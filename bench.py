@@ -49,6 +49,14 @@ def parse():
     p.add_argument("--unfused", action="store_true",
                    help="time the step as three launches (pa_kv_append, "
                         "then pa_decode) instead of pa_decode_append")
+    p.add_argument("--op", default="step",
+                   choices=["step", "append", "append_quant"],
+                   help="step: the decode step (default); append / "
+                        "append_quant: writing --tokens new tokens into the "
+                        "workload's pool (bf16 copy, or bf16 -> fp8 e4m3fn "
+                        "quantisation)")
+    p.add_argument("--tokens", type=int, default=32768,
+                   help="tokens written per launch by --op append*")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the bench, run three plain 1 GiB device "
                         "copies (the reference kernel that scales HBM "
@@ -125,6 +133,104 @@ def cpu_baseline(case, budget_s: float):
     }
 
 
+def _kernel_events(torch, n):
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    return ev
+
+
+def bench_append(a, torch, _lib):
+    """Throughput of writing many new tokens into a pool (a prefill chunk's
+    KV): --op append copies bf16 rows into a bf16 pool, --op append_quant
+    quantises bf16 rows into an fp8 e4m3fn pool.  Slots are a seeded random
+    set of distinct slots of the pool, so rows land in scattered blocks."""
+    import numpy as np
+
+    quant = a.op == "append_quant"
+    nb_needed = -(-a.tokens // 16)
+    nb = nb_needed + nb_needed // 10 + 1
+    hkv, d = 8, 128
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(a.seed or 0)
+    k_new = torch.randn(a.tokens, hkv, d, generator=g).to(torch.bfloat16)
+    v_new = torch.randn(a.tokens, hkv, d, generator=g).to(torch.bfloat16)
+    slots = torch.from_numpy(np.random.default_rng(a.seed or 0).permutation(
+        nb * 16)[:a.tokens].astype(np.int32))
+    pool_dtype = torch.float8_e4m3fn if quant else torch.bfloat16
+    kp = torch.zeros(nb, hkv, 16, d, dtype=torch.uint8 if quant
+                     else torch.bfloat16, device=dev).view(pool_dtype)
+    vp = torch.zeros(nb, hkv, d, 16, dtype=torch.uint8 if quant
+                     else torch.bfloat16, device=dev).view(pool_dtype)
+    kn, vn, sl = k_new.to(dev), v_new.to(dev), slots.to(dev)
+    ks = float(np.float32(4.5 / 448))
+    vs = float(np.float32(4.5 / 448))
+
+    def call():
+        if quant:
+            _lib.pa_kv_append_quant(kn, vn, sl, kp, vp, ks, vs)
+        else:
+            _lib.pa_kv_append(kn, vn, sl, kp, vp)
+
+    for _ in range(a.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = _kernel_events(torch, a.steps)
+    for e0, e1 in ev:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    avg = sum(ms) / len(ms)
+    out_bytes = 1 if quant else 2
+    nbytes = a.tokens * hkv * d * 2 * (2 + out_bytes) + 4 * a.tokens
+    gbs = nbytes / (avg * 1e-3) / 1e9
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle
+        from oracle import quant as oquant
+        n_s = min(a.tokens, 4096)
+        kp_h = np.zeros((nb, hkv, 16, d), dtype=np.uint8 if quant
+                        else np.uint16)
+        vp_h = np.zeros((nb, hkv, d, 16), dtype=kp_h.dtype)
+        knb = k_new[:n_s].view(torch.uint16).numpy()
+        vnb = v_new[:n_s].view(torch.uint16).numpy()
+        t0 = time.perf_counter()
+        if quant:
+            oquant.kv_append_quant(kp_h, vp_h, knb, vnb, slots[:n_s].numpy(),
+                                   ks, vs)
+        else:
+            oracle.kv_append(kp_h, vp_h, knb, vnb, slots[:n_s].numpy())
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(n_s * hkv * d * 2 * (2 + out_bytes) / dt / 1e9,
+                              4),
+               "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the oracle's append of the first {n_s} of the "
+                         f"tokens into host copies of the pools "
+                         f"({dt:.2f} s, including the oracle's copy of the host "
+                         f"pools)"}
+    print(json.dumps({
+        "metric": ("quantising KV append (bf16 -> fp8 e4m3fn): HBM GB/s"
+                   if quant else "KV append (bf16): HBM GB/s"),
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(avg, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->fp8" if quant else "bf16", "data": "synthetic",
+        "config": {"workload": f"append {a.tokens} tokens", "tokens": a.tokens,
+                   "num_kv_heads": hkv, "head_size": d, "pool_blocks": nb},
+        "roofline": {"bound": "hbm", "kernel": "kv_append_quant_kernel"
+                     if quant else "kv_append_kernel",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+                     "kernel_ms_avg": round(avg, 5),
+                     "kernel_ms_median": round(ms[len(ms) // 2], 5)},
+        "cpu_baseline": cpu,
+    }), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -143,6 +249,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     _lib.load()
+    if a.op != "step":
+        bench_append(a, torch, _lib)
+        return
     cfg = CONFIG_BY_NAME[a.config]
     seed = a.seed if a.seed is not None else \
         [c.name for c in CONFIGS].index(cfg.name)

@@ -230,6 +230,24 @@ int pa_kv_append(const void* k_new, const void* v_new,
                  const int32_t* slot_mapping, void* k_pool, void* v_pool,
                  const pa_append_desc* desc, void* stream);
 
+/*
+ * Quantising append into an fp8 pool: like pa_kv_append, but k_new / v_new
+ * are bfloat16 [N][Hkv][D] and each value is stored as the e4m3fn code of
+ * value / scale, with k_scale for K and v_scale for V (the pool's
+ * per-tensor scales: stored value * scale = real value).  FP8 storage
+ * halves a block's bytes ("PagedAttention：KV cache 即虚拟内存", section
+ * "面试官追问").  The code is the nearest e4m3fn value of the IEEE float32
+ * quotient, ties to the even code, magnitudes above 448 saturated to 448,
+ * NaN stored as 0x7F, the sign of zero kept.
+ *   desc->kv_dtype must be PA_FP8_E4M3FN (the pool's type); scales must be
+ *   finite and > 0 (else PA_ERR_SHAPE).  Pointers, slots and errors as for
+ *   pa_kv_append.
+ */
+int pa_kv_append_quant(const void* k_new, const void* v_new,
+                       const int32_t* slot_mapping, void* k_pool,
+                       void* v_pool, const pa_append_desc* desc,
+                       float k_scale, float v_scale, void* stream);
+
 /* Static English text of a pa_status value. */
 const char* pa_status_string(int status);
 

@@ -15,11 +15,13 @@ Modules:
 * ``append``   - byte copy of new tokens' K/V into their pool slots.
 * ``capacity`` - the block/byte arithmetic and the contiguous-vs-paged
   capacity example.
+* ``quant``    - the quantising append into an fp8 e4m3fn pool (nearest
+  e4m3fn value of x / scale, saturating, ties to even).
 
-Every function is pinned by ``tests/test_oracle.py`` against library
-routines, closed forms, invariants, brute force and the pages' printed
-example; none is "parity unpinned".
+Every function is pinned by ``tests/test_oracle.py`` and
+``tests/test_quant.py`` against library routines, closed forms, invariants,
+brute force and the pages' printed example; none is "parity unpinned".
 """
-from . import append, capacity, decode, numerics  # noqa: F401
+from . import append, capacity, decode, numerics, quant  # noqa: F401
 from .append import kv_append  # noqa: F401
 from .decode import paged_decode, attention_weights  # noqa: F401

@@ -26,7 +26,7 @@ _DTYPE = {
 # names every build of the library exports (checked by the tests)
 EXPORTS = ("pa_decode", "pa_decode_workspace_size", "pa_decode_append",
            "pa_decode_append_workspace_size", "pa_kv_append",
-           "pa_status_string", "pa_abi_version")
+           "pa_kv_append_quant", "pa_status_string", "pa_abi_version")
 
 
 class DecodeDesc(ctypes.Structure):
@@ -90,6 +90,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_kv_append.argtypes = [vp, vp, vp, vp, vp,
                                  ctypes.POINTER(AppendDesc), vp]
     lib.pa_kv_append.restype = ctypes.c_int
+    lib.pa_kv_append_quant.argtypes = [vp, vp, vp, vp, vp,
+                                       ctypes.POINTER(AppendDesc),
+                                       ctypes.c_float, ctypes.c_float, vp]
+    lib.pa_kv_append_quant.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_abi_version.argtypes = []
@@ -211,6 +215,23 @@ def pa_kv_append(k_new, v_new, slot_mapping, k_pool, v_pool) -> None:
     _check(lib.pa_kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
                             _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
                             _stream()))
+
+
+def pa_kv_append_quant(k_new, v_new, slot_mapping, k_pool, v_pool,
+                       k_scale: float, v_scale: float) -> None:
+    """Write bf16 rows into an fp8 e4m3fn pool as value / scale codes (see
+    ``include/pa.h``)."""
+    lib = load()
+    if k_new.dtype != torch.bfloat16 or k_pool.dtype != torch.float8_e4m3fn:
+        raise ValueError("pa_kv_append_quant takes bf16 rows and fp8 pools")
+    n, hkv, d = k_new.shape
+    desc = AppendDesc(num_tokens=n, num_kv_heads=hkv, head_size=d,
+                      block_size=k_pool.shape[2], num_blocks=k_pool.shape[0],
+                      kv_dtype=PA_FP8_E4M3FN)
+    _check(lib.pa_kv_append_quant(
+        _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_pool),
+        _ptr(v_pool), ctypes.byref(desc), ctypes.c_float(k_scale),
+        ctypes.c_float(v_scale), _stream()))
 
 
 class PreparedStep:

@@ -305,4 +305,37 @@ int pa_kv_append(const void* k_new, const void* v_new,
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+int pa_kv_append_quant(const void* k_new, const void* v_new,
+                       const int32_t* slot_mapping, void* k_pool,
+                       void* v_pool, const pa_append_desc* desc,
+                       float k_scale, float v_scale, void* stream) {
+  if (!desc) return PA_ERR_NULL;
+  if (desc->num_tokens < 0 || desc->num_kv_heads < 1 ||
+      !head_size_ok(desc->head_size) || desc->block_size != pa::kBlock ||
+      desc->num_blocks < 1 ||
+      (int64_t)desc->num_blocks * pa::kBlock > INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (desc->kv_dtype != PA_FP8_E4M3FN) return PA_ERR_DTYPE;
+  if (!(k_scale > 0.f && v_scale > 0.f && isfinite(k_scale) &&
+        isfinite(v_scale)))
+    return PA_ERR_SHAPE;
+  if ((int64_t)desc->num_kv_heads * desc->head_size > INT32_MAX / 16 ||
+      (int64_t)desc->num_tokens *
+              pa::append_workgroups_per_token(2, desc->num_kv_heads,
+                                              desc->head_size) >
+          INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (desc->num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool)
+    return PA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) ||
+      !aligned16(v_pool) || ((uintptr_t)slot_mapping & 3u))
+    return PA_ERR_ALIGN;
+  hipError_t e = pa::launch_kv_append_quant(
+      k_new, v_new, slot_mapping, k_pool, v_pool, desc->num_tokens,
+      desc->num_kv_heads, desc->head_size, desc->num_blocks, k_scale,
+      v_scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 }  // extern "C"

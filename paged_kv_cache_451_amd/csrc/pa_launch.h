@@ -64,4 +64,14 @@ hipError_t launch_kv_append(int elem_bytes, const void* k_new,
                             int num_kv_heads, int head_size, int num_blocks,
                             hipStream_t stream);
 
+// Quantising append: bf16 rows into an fp8 e4m3fn pool (value / scale,
+// nearest e4m3fn code, ties to even, saturating at 448).  Same grid as
+// launch_kv_append with 2-byte input elements.
+hipError_t launch_kv_append_quant(const void* k_new, const void* v_new,
+                                  const int32_t* slots, void* k_pool,
+                                  void* v_pool, int num_tokens,
+                                  int num_kv_heads, int head_size,
+                                  int num_blocks, float k_scale,
+                                  float v_scale, hipStream_t stream);
+
 }  // namespace pa

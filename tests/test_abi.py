@@ -151,6 +151,26 @@ def test_null_pointers_and_alignment_are_rejected(lib):
     assert lib.pa_kv_append(p, p, p, p, p, ctypes.byref(a), None) == -3
 
 
+def test_quantising_append_checks(lib):
+    p, odd = ctypes.c_void_p(256), ctypes.c_void_p(258)
+    a = _lib.AppendDesc(num_tokens=1, num_kv_heads=2, head_size=64,
+                        block_size=16, num_blocks=4,
+                        kv_dtype=_lib.PA_FP8_E4M3FN)
+    one = ctypes.c_float(1.0)
+    q = lib.pa_kv_append_quant
+    assert q(None, p, p, p, p, ctypes.byref(a), one, one, None) == -1
+    assert q(odd, p, p, p, p, ctypes.byref(a), one, one, None) == -4
+    assert q(p, p, p, p, p, ctypes.byref(a), ctypes.c_float(0.0), one,
+             None) == -3
+    assert q(p, p, p, p, p, ctypes.byref(a), one,
+             ctypes.c_float(float("inf")), None) == -3
+    a.kv_dtype = _lib.PA_BF16
+    assert q(p, p, p, p, p, ctypes.byref(a), one, one, None) == -2
+    a.kv_dtype, a.num_tokens = _lib.PA_FP8_E4M3FN, 0
+    assert q(None, None, None, None, None, ctypes.byref(a), one, one,
+             None) == 0
+
+
 def test_empty_calls_are_no_ops(lib):
     d = _desc(num_seqs=0)
     assert lib.pa_decode_workspace_size(ctypes.byref(d)) == 0

@@ -417,3 +417,51 @@ def test_fused_step_single_token_sequences(gpu_lib):
     expect = np.repeat(vn, 4, axis=1)
     assert np.abs(out[:2].cpu().to(torch.float64).numpy() -
                   expect[:2]).max() <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# quantising append (bf16 rows into an fp8 e4m3fn pool): bit-exact
+# ---------------------------------------------------------------------------
+def _quant_append_check(k_new, v_new, slots, k_pool, v_pool, ks, vs):
+    from oracle import quant
+    from paged_kv_cache_451_amd import _lib
+    kp, vp = k_pool.cuda(), v_pool.cuda()
+    _lib.pa_kv_append_quant(k_new.cuda(), v_new.cuda(), slots.cuda(), kp, vp,
+                            ks, vs)
+    torch.cuda.synchronize()
+    k1, v1 = quant.kv_append_quant(
+        raw_bits(k_pool).reshape(k_pool.shape),
+        raw_bits(v_pool).reshape(v_pool.shape),
+        k_new.view(torch.uint16).numpy(), v_new.view(torch.uint16).numpy(),
+        slots.numpy(), ks, vs)
+    assert np.array_equal(raw_bits(kp).ravel(), k1.ravel())
+    assert np.array_equal(raw_bits(vp).ravel(), v1.ravel())
+
+
+@pytest.mark.parametrize("ks, vs", [(1.0, 1.0), (0.0123, 1.0 / 448),
+                                    (3.7, 0.5)])
+def test_quantising_append_every_bf16_code(gpu_lib, ks, vs):
+    """All 65536 bf16 codes (NaN, infinities, subnormals, every e4m3fn tie
+    that bf16 can hold at scale 1) as K and, reversed, as V."""
+    hkv, d, n, nb = 8, 128, 64, 80
+    codes = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16)
+    k_new = codes.view(torch.bfloat16).reshape(n, hkv, d).contiguous()
+    v_new = k_new.flip(0).contiguous()
+    g = torch.Generator().manual_seed(17)
+    k_pool = torch.randint(0, 256, (nb, hkv, 16, d), generator=g,
+                           dtype=torch.uint8).view(torch.float8_e4m3fn)
+    v_pool = torch.randint(0, 256, (nb, hkv, d, 16), generator=g,
+                           dtype=torch.uint8).view(torch.float8_e4m3fn)
+    slots = torch.randperm(nb * 16, generator=g)[:n].to(torch.int32)
+    slots[3] = -1
+    _quant_append_check(k_new, v_new, slots, k_pool, v_pool, ks, vs)
+
+
+def test_quantising_append_full_fp8_workload(gpu_lib):
+    case = full_case("fp8_long")
+    g = torch.Generator().manual_seed(5)
+    shape = tuple(case.k_new.shape)
+    k_new = torch.randn(shape, generator=g).to(torch.bfloat16)
+    v_new = (torch.randn(shape, generator=g) * 3).to(torch.bfloat16)
+    _quant_append_check(k_new, v_new, case.slot_mapping, case.k_pool,
+                        case.v_pool, case.k_scale, case.v_scale)
