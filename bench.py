@@ -50,11 +50,15 @@ def parse():
                    help="time the step as three launches (pa_kv_append, "
                         "then pa_decode) instead of pa_decode_append")
     p.add_argument("--op", default="step",
-                   choices=["step", "append", "append_quant"],
+                   choices=["step", "append", "append_quant",
+                            "copy_blocks"],
                    help="step: the decode step (default); append / "
-                        "append_quant: writing --tokens new tokens into the "
-                        "workload's pool (bf16 copy, or bf16 -> fp8 e4m3fn "
-                        "quantisation)")
+                        "append_quant: writing --tokens new tokens into a "
+                        "pool (bf16 copy, or bf16 -> fp8 e4m3fn "
+                        "quantisation); copy_blocks: copy-on-write of "
+                        "--pairs whole blocks")
+    p.add_argument("--pairs", type=int, default=4096,
+                   help="block pairs copied per launch by --op copy_blocks")
     p.add_argument("--tokens", type=int, default=32768,
                    help="tokens written per launch by --op append*")
     p.add_argument("--copy-calibration", action="store_true",
@@ -231,6 +235,71 @@ def bench_append(a, torch, _lib):
     }), flush=True)
 
 
+def bench_copy_blocks(a, torch, _lib):
+    """Throughput of copy-on-write block copies: --pairs distinct source
+    blocks copied to distinct destination blocks of a bf16 pool shaped like
+    the Llama-3-8B workload (8 KV heads, head size 128: 32 KiB per block and
+    pool)."""
+    import numpy as np
+
+    hkv, d = 8, 128
+    nb = 2 * a.pairs + 16
+    dev = torch.device("cuda:0")
+    kp = torch.empty(nb, hkv, 16, d, dtype=torch.bfloat16, device=dev)
+    vp = torch.empty(nb, hkv, d, 16, dtype=torch.bfloat16, device=dev)
+    kp.normal_()
+    vp.normal_()
+    perm = np.random.default_rng(a.seed or 0).permutation(nb)
+    src = torch.from_numpy(perm[:a.pairs].astype(np.int32)).to(dev)
+    dst = torch.from_numpy(perm[a.pairs:2 * a.pairs].astype(np.int32)).to(dev)
+    for _ in range(a.warmup):
+        _lib.pa_copy_blocks(kp, vp, src, dst)
+    torch.cuda.synchronize()
+    ev = _kernel_events(torch, a.steps)
+    for e0, e1 in ev:
+        e0.record()
+        _lib.pa_copy_blocks(kp, vp, src, dst)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    avg = sum(ms) / len(ms)
+    block = hkv * 16 * d * 2
+    nbytes = a.pairs * 2 * block * 2 + 8 * a.pairs
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle
+        n_s = min(a.pairs, 256)
+        kh = kp[:2 * n_s + 16].cpu().view(torch.uint16).numpy()
+        vh = vp[:2 * n_s + 16].cpu().view(torch.uint16).numpy()
+        ps = np.random.default_rng(1).permutation(2 * n_s + 16)
+        t0 = time.perf_counter()
+        oracle.append.copy_blocks(kh, vh, ps[:n_s], ps[n_s:2 * n_s])
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(n_s * 2 * block * 2 / dt / 1e9, 4),
+               "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the oracle's copy of {n_s} block pairs on host "
+                         f"copies of the pools ({dt:.3f} s, including the "
+                         f"oracle's copy of the host pools)"}
+    print(json.dumps({
+        "metric": "copy-on-write block copy: HBM GB/s (read + write)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(avg, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"copy {a.pairs} block pairs",
+                   "pairs": a.pairs, "num_kv_heads": hkv, "head_size": d,
+                   "block_bytes_per_pool": block},
+        "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+                     "kernel_ms_avg": round(avg, 5),
+                     "kernel_ms_median": round(ms[len(ms) // 2], 5)},
+        "cpu_baseline": cpu,
+    }), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -249,6 +318,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     _lib.load()
+    if a.op == "copy_blocks":
+        bench_copy_blocks(a, torch, _lib)
+        return
     if a.op != "step":
         bench_append(a, torch, _lib)
         return

@@ -248,6 +248,43 @@ int pa_kv_append_quant(const void* k_new, const void* v_new,
                        void* v_pool, const pa_append_desc* desc,
                        float k_scale, float v_scale, void* stream);
 
+/*
+ * Shapes of one block copy.
+ *   num_pairs     P >= 0
+ *   num_kv_heads, head_size, block_size (16), num_blocks, kv_dtype: the
+ *                 pools' shape and element type, as for pa_kv_append
+ */
+typedef struct {
+  int32_t num_pairs;
+  int32_t num_kv_heads;
+  int32_t head_size;
+  int32_t block_size;
+  int32_t num_blocks;
+  pa_dtype kv_dtype;
+} pa_copy_desc;
+
+/*
+ * Copy-on-write of shared blocks: for every i < P, K block src_blocks[i]
+ * and V block src_blocks[i] (all KV heads, all 16 slots) are copied byte
+ * for byte to block dst_blocks[i] of the same pools.  The block manager
+ * issues these when a sequence appends into a block another sequence still
+ * references: sharing is copy-on-write, and a diverging sequence gets its
+ * own copy of the block first ("49 vLLM / PagedAttention", section "Почему
+ * это важно"; "PagedAttention：KV cache 即虚拟内存", section "深入原理",
+ * sharing bullet).
+ *   k_pool, v_pool          16-byte aligned pools (layouts as above).
+ *   src_blocks, dst_blocks  int32 [P], device memory.  Destinations must be
+ *                           distinct and must not appear as sources of the
+ *                           same call (else the result is unspecified);
+ *                           pairs with an id outside [0, num_blocks) are
+ *                           skipped.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_ALIGN,
+ * PA_ERR_LAUNCH, as for pa_kv_append.
+ */
+int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_blocks,
+                   const int32_t* dst_blocks, const pa_copy_desc* desc,
+                   void* stream);
+
 /* Static English text of a pa_status value. */
 const char* pa_status_string(int status);
 

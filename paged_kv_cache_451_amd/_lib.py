@@ -26,7 +26,8 @@ _DTYPE = {
 # names every build of the library exports (checked by the tests)
 EXPORTS = ("pa_decode", "pa_decode_workspace_size", "pa_decode_append",
            "pa_decode_append_workspace_size", "pa_kv_append",
-           "pa_kv_append_quant", "pa_status_string", "pa_abi_version")
+           "pa_kv_append_quant", "pa_copy_blocks", "pa_status_string",
+           "pa_abi_version")
 
 
 class DecodeDesc(ctypes.Structure):
@@ -53,6 +54,17 @@ class DecodeDesc(ctypes.Structure):
 class AppendDesc(ctypes.Structure):
     _fields_ = [
         ("num_tokens", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int),
+    ]
+
+
+class CopyDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_pairs", ctypes.c_int32),
         ("num_kv_heads", ctypes.c_int32),
         ("head_size", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
@@ -94,6 +106,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        ctypes.POINTER(AppendDesc),
                                        ctypes.c_float, ctypes.c_float, vp]
     lib.pa_kv_append_quant.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, ctypes.POINTER(CopyDesc),
+                                   vp]
+    lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_abi_version.argtypes = []
@@ -232,6 +247,21 @@ def pa_kv_append_quant(k_new, v_new, slot_mapping, k_pool, v_pool,
         _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_pool),
         _ptr(v_pool), ctypes.byref(desc), ctypes.c_float(k_scale),
         ctypes.c_float(v_scale), _stream()))
+
+
+def pa_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks) -> None:
+    """Copy whole K/V blocks src -> dst (copy-on-write; see
+    ``include/pa.h``)."""
+    lib = load()
+    nb, hkv, bs, d = k_pool.shape
+    desc = CopyDesc(num_pairs=src_blocks.numel(), num_kv_heads=hkv,
+                    head_size=d, block_size=bs, num_blocks=nb,
+                    kv_dtype=_DTYPE[k_pool.dtype])
+    if dst_blocks.numel() != src_blocks.numel():
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    _check(lib.pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(src_blocks),
+                              _ptr(dst_blocks), ctypes.byref(desc),
+                              _stream()))
 
 
 class PreparedStep:

@@ -1,0 +1,74 @@
+// Block copy for copy-on-write: for every pair i, the whole K block and the
+// whole V block src[i] (all KV heads) are copied to block dst[i].  A block
+// of one pool is Hkv * 16 * D contiguous elements, so a pair is two
+// contiguous byte ranges.  Each workgroup copies kChunksPerThread 16-byte
+// chunks per thread of one pair; all loads are issued before the stores.
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCopyThreads = 256;
+constexpr int kChunksPerThread = 4;
+constexpr int kChunksPerGroup = kCopyThreads * kChunksPerThread;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+    int num_blocks, int chunks_per_block, int wpp) {
+  const int i = blockIdx.x / wpp;
+  const int part = blockIdx.x - i * wpp;
+  const int s = src[i];
+  const int t = dst[i];
+  if ((unsigned)s >= (unsigned)num_blocks ||
+      (unsigned)t >= (unsigned)num_blocks)
+    return;
+  const size_t block_bytes = (size_t)chunks_per_block * 16;
+  u32x4 val[kChunksPerThread];
+  bool live[kChunksPerThread];
+#pragma unroll
+  for (int u = 0; u < kChunksPerThread; ++u) {
+    const int c = part * kChunksPerGroup + u * kCopyThreads + threadIdx.x;
+    live[u] = c < 2 * chunks_per_block;
+    const bool is_v = c >= chunks_per_block;
+    const uint8_t* base = is_v ? v_pool : k_pool;
+    const size_t off = (size_t)(is_v ? c - chunks_per_block : c) * 16;
+    if (live[u])
+      val[u] = *reinterpret_cast<const u32x4*>(base + (size_t)s * block_bytes +
+                                               off);
+  }
+#pragma unroll
+  for (int u = 0; u < kChunksPerThread; ++u) {
+    const int c = part * kChunksPerGroup + u * kCopyThreads + threadIdx.x;
+    const bool is_v = c >= chunks_per_block;
+    uint8_t* base = is_v ? v_pool : k_pool;
+    const size_t off = (size_t)(is_v ? c - chunks_per_block : c) * 16;
+    if (live[u])
+      *reinterpret_cast<u32x4*>(base + (size_t)t * block_bytes + off) = val[u];
+  }
+}
+
+}  // namespace
+
+int copy_workgroups_per_pair(int block_bytes) {
+  const int chunks = 2 * (block_bytes / 16);
+  return (chunks + kChunksPerGroup - 1) / kChunksPerGroup;
+}
+
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* src,
+                              const int32_t* dst, int num_pairs,
+                              int block_bytes, int num_blocks,
+                              hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const int wpp = copy_workgroups_per_pair(block_bytes);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)(num_pairs * wpp)),
+                     dim3(kCopyThreads), 0, stream,
+                     reinterpret_cast<uint8_t*>(k_pool),
+                     reinterpret_cast<uint8_t*>(v_pool), src, dst,
+                     num_blocks, block_bytes / 16, wpp);
+  return hipGetLastError();
+}
+
+}  // namespace pa

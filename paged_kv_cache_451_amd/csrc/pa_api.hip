@@ -338,4 +338,32 @@ int pa_kv_append_quant(const void* k_new, const void* v_new,
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_blocks,
+                   const int32_t* dst_blocks, const pa_copy_desc* desc,
+                   void* stream) {
+  if (!desc) return PA_ERR_NULL;
+  if (desc->num_pairs < 0 || desc->num_kv_heads < 1 ||
+      !head_size_ok(desc->head_size) || desc->block_size != pa::kBlock ||
+      desc->num_blocks < 1)
+    return PA_ERR_SHAPE;
+  const size_t eb = dtype_bytes(desc->kv_dtype);
+  if (eb == 0) return PA_ERR_DTYPE;
+  const int64_t block_bytes =
+      (int64_t)desc->num_kv_heads * pa::kBlock * desc->head_size * (int64_t)eb;
+  if (block_bytes > INT32_MAX / 2) return PA_ERR_SHAPE;
+  if ((int64_t)desc->num_pairs *
+          pa::copy_workgroups_per_pair((int)block_bytes) >
+      INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (desc->num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !src_blocks || !dst_blocks) return PA_ERR_NULL;
+  if (!aligned16(k_pool) || !aligned16(v_pool) ||
+      ((uintptr_t)src_blocks & 3u) || ((uintptr_t)dst_blocks & 3u))
+    return PA_ERR_ALIGN;
+  hipError_t e = pa::launch_copy_blocks(
+      k_pool, v_pool, src_blocks, dst_blocks, desc->num_pairs,
+      (int)block_bytes, desc->num_blocks, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -74,4 +74,13 @@ hipError_t launch_kv_append_quant(const void* k_new, const void* v_new,
                                   int num_blocks, float k_scale,
                                   float v_scale, hipStream_t stream);
 
+// Copy-on-write block copy: K and V block src[i] -> dst[i] for every pair
+// (block_bytes per pool block, a multiple of 16).  Pairs with an id outside
+// [0, num_blocks) are skipped.
+int copy_workgroups_per_pair(int block_bytes);
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* src,
+                              const int32_t* dst, int num_pairs,
+                              int block_bytes, int num_blocks,
+                              hipStream_t stream);
+
 }  // namespace pa

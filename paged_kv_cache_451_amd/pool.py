@@ -22,6 +22,14 @@ What the pages describe, restated:
   ``touch()`` raises the reference count of a block another request already
   holds.  ("PagedAttention：KV cache 即虚拟内存", section "深入原理", bullet on
   sharing / prefix caching.)
+* Prefix caching: a full block is keyed by a hash of its tokens and of its
+  parent block's hash, kept in ``cached_block_hash_to_block``; a request
+  whose leading full blocks hash to cached blocks points at them instead of
+  recomputing them.  Only full blocks are cached, so identical prefixes give
+  byte-identical KV and unchanged output; when sequences diverge inside a
+  shared block, that block is copied first (copy-on-write).  (Same bullet;
+  "49 vLLM / PagedAttention", sections "Почему это важно" and "Вопросы
+  пытливого ума".)
 
 Readings taken where the pages leave a step open:
 
@@ -32,17 +40,26 @@ Readings taken where the pages leave a step open:
   does not fit (the scheduler queues once the pool is full).  With this rule
   the pages' capacity example gives 13 paged sequences; admitting later,
   smaller requests past a miss gives 14.
-* A finished sequence returns its blocks in table order.
-* Appending into a block with ``ref_cnt > 1`` would need copy-on-write, which
-  this harness does not implement: it raises instead.
+* A finished sequence returns its blocks in table order.  A freed block
+  keeps its hash and stays findable until allocation pops it from the free
+  queue (the queue is in eviction order), which evicts it from the cache.
+* The block hash is the first 8 bytes of SHA-256 over the parent's hash
+  and the block's token ids (both as little-endian 64-bit integers); the
+  first block's parent hash is 0.  Lookups stop at the first miss.
+* Copy-on-write: appending into a block with ``ref_cnt > 1`` takes a fresh
+  block, records the (source, destination) pair for the device copy
+  (``pa_copy_blocks``), drops one reference to the source and continues in
+  the copy.
 
 Pure host logic (Python, no GPU): it builds the int32 ``block_tables``,
 ``seq_lens`` and ``slot_mapping`` arrays the device entry points consume.
 """
 from __future__ import annotations
 
+import hashlib
+import struct
 from dataclasses import dataclass, field
-from typing import Dict, Iterable, List, Optional, Sequence
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -50,7 +67,8 @@ import numpy as np
 class KVCacheBlock:
     """One physical block of the pool (``block_id`` indexes the pool tensors)."""
 
-    __slots__ = ("block_id", "ref_cnt", "prev", "next", "in_free_queue")
+    __slots__ = ("block_id", "ref_cnt", "prev", "next", "in_free_queue",
+                 "block_hash")
 
     def __init__(self, block_id: int):
         self.block_id = block_id
@@ -58,6 +76,7 @@ class KVCacheBlock:
         self.prev: Optional[KVCacheBlock] = None
         self.next: Optional[KVCacheBlock] = None
         self.in_free_queue = False
+        self.block_hash: Optional[int] = None
 
     def __repr__(self) -> str:  # pragma: no cover - debugging aid
         return f"KVCacheBlock(id={self.block_id}, ref_cnt={self.ref_cnt})"
@@ -114,6 +133,13 @@ class FreeBlockQueue:
         return out
 
 
+def hash_block_tokens(parent_hash: int, token_ids: Sequence[int]) -> int:
+    """Key of a full block: its token ids chained to its parent's key."""
+    h = hashlib.sha256(struct.pack("<Q", parent_hash & (2**64 - 1)))
+    h.update(np.asarray(token_ids, dtype="<i8").tobytes())
+    return int.from_bytes(h.digest()[:8], "little")
+
+
 class BlockPool:
     """Owns every ``KVCacheBlock``; hands them out from the free queue.
 
@@ -132,19 +158,35 @@ class BlockPool:
         if sorted(order) != list(range(num_blocks)):
             raise ValueError("order must be a permutation of range(num_blocks)")
         self.free_block_queue = FreeBlockQueue(self.blocks[i] for i in order)
+        self.cached_block_hash_to_block: Dict[int, KVCacheBlock] = {}
 
     @property
     def num_free(self) -> int:
         return len(self.free_block_queue)
 
     def alloc(self) -> Optional[KVCacheBlock]:
-        """Pop the head of the free queue (None when the pool is exhausted)."""
+        """Pop the head of the free queue (None when the pool is exhausted).
+        A popped block that was still cached is evicted from the cache."""
         block = self.free_block_queue.popleft()
         if block is None:
             return None
         assert block.ref_cnt == 0
+        if block.block_hash is not None:
+            if self.cached_block_hash_to_block.get(block.block_hash) is block:
+                del self.cached_block_hash_to_block[block.block_hash]
+            block.block_hash = None
         block.ref_cnt = 1
         return block
+
+    def lookup(self, block_hash: int) -> Optional[KVCacheBlock]:
+        return self.cached_block_hash_to_block.get(block_hash)
+
+    def cache(self, block: KVCacheBlock, block_hash: int) -> None:
+        """Register a full block under its key (first one wins)."""
+        if block.block_hash is None and \
+                block_hash not in self.cached_block_hash_to_block:
+            block.block_hash = block_hash
+            self.cached_block_hash_to_block[block_hash] = block
 
     def touch(self, block: KVCacheBlock) -> None:
         """Another request starts sharing ``block``."""
@@ -166,6 +208,7 @@ class SeqState:
     seq_id: int
     num_tokens: int = 0  # tokens already stored in the cache
     blocks: List[KVCacheBlock] = field(default_factory=list)
+    token_ids: Optional[List[int]] = None  # kept when prefix caching is used
 
 
 class KVCacheManager:
@@ -177,6 +220,9 @@ class KVCacheManager:
         self.pool = pool
         self.block_size = block_size
         self.req_to_blocks: Dict[int, SeqState] = {}
+        # (source, destination) block pairs the device must copy before the
+        # next append (copy-on-write); drained by take_copies()
+        self.pending_copies: List[Tuple[int, int]] = []
 
     # -- admission -----------------------------------------------------------
     def blocks_needed(self, num_tokens: int) -> int:
@@ -211,6 +257,63 @@ class KVCacheManager:
         self.req_to_blocks[seq_id] = state
         return True
 
+    def admit_cached(self, seq_id: int,
+                     token_ids: Sequence[int]) -> Tuple[bool, int]:
+        """Admit a request whose tokens are known, reusing cached full
+        blocks of an identical prefix.  Returns (admitted, cached blocks
+        reused); the reused blocks' KV is already in the pool, only the rest
+        must be written.  Fresh full blocks are registered in the cache."""
+        if seq_id in self.req_to_blocks:
+            raise ValueError(f"sequence {seq_id} already admitted")
+        bs = self.block_size
+        toks = [int(t) for t in token_ids]
+        nfull = len(toks) // bs
+        hashes, parent = [], 0
+        for i in range(nfull):
+            parent = hash_block_tokens(parent, toks[i * bs:(i + 1) * bs])
+            hashes.append(parent)
+        hits: List[KVCacheBlock] = []
+        for h in hashes:
+            blk = self.pool.lookup(h)
+            if blk is None:
+                break
+            hits.append(blk)
+        # a hit that sits in the free queue still counts as free until
+        # touched: it must not be allocated for this request's fresh blocks
+        fresh = self.blocks_needed(len(toks)) - len(hits)
+        free_hits = sum(1 for b in hits if b.ref_cnt == 0)
+        if fresh > self.pool.num_free - free_hits:
+            return False, 0
+        state = SeqState(seq_id, token_ids=list(toks))
+        for blk in hits:
+            self.pool.touch(blk)
+            state.blocks.append(blk)
+        for i in range(fresh):
+            blk = self.pool.alloc()
+            state.blocks.append(blk)
+            j = len(hits) + i
+            if j < nfull:
+                self.pool.cache(blk, hashes[j])
+        state.num_tokens = len(toks)
+        self.req_to_blocks[seq_id] = state
+        return True, len(hits)
+
+    def fork(self, src_id: int, new_id: int) -> None:
+        """A new sequence continuing src's context: it shares every block
+        (parallel sampling, beam search); divergence is copy-on-write."""
+        if new_id in self.req_to_blocks:
+            raise ValueError(f"sequence {new_id} already admitted")
+        src = self.req_to_blocks[src_id]
+        for blk in src.blocks:
+            self.pool.touch(blk)
+        self.req_to_blocks[new_id] = SeqState(
+            new_id, src.num_tokens, list(src.blocks),
+            None if src.token_ids is None else list(src.token_ids))
+
+    def take_copies(self) -> List[Tuple[int, int]]:
+        out, self.pending_copies = self.pending_copies, []
+        return out
+
     def admit_fcfs(self, lengths: Sequence[int]) -> int:
         """Admit requests in arrival order; stop at the first that does not fit."""
         admitted = 0
@@ -221,24 +324,42 @@ class KVCacheManager:
         return admitted
 
     # -- growth --------------------------------------------------------------
-    def append_slot(self, seq_id: int) -> int:
+    def append_slot(self, seq_id: int, token_id: Optional[int] = None) -> int:
         """Reserve the slot of one new token (allocate-on-growth).
 
         A block is popped only when every slot of the existing blocks is used.
-        Returns the flat slot ``phys * block_size + offset``; raises when the
-        pool is exhausted or the target block is shared.
+        If the target block is shared, it is copied first (copy-on-write: the
+        pair is queued in ``pending_copies``).  Returns the flat slot
+        ``phys * block_size + offset``; raises MemoryError when the pool is
+        exhausted.  With prefix caching (token ids known), a block that the
+        token fills up is registered in the cache.
         """
         st = self.req_to_blocks[seq_id]
-        if len(st.blocks) * self.block_size <= st.num_tokens:
+        bs = self.block_size
+        if len(st.blocks) * bs <= st.num_tokens:
             blk = self.pool.alloc()
             if blk is None:
                 raise MemoryError("KV block pool exhausted")
             st.blocks.append(blk)
-        last = st.blocks[st.num_tokens // self.block_size]
+        idx = st.num_tokens // bs
+        last = st.blocks[idx]
         if last.ref_cnt > 1:
-            raise RuntimeError("append into a shared block needs copy-on-write")
-        slot = last.block_id * self.block_size + st.num_tokens % self.block_size
+            copy = self.pool.alloc()
+            if copy is None:
+                raise MemoryError("KV block pool exhausted (copy-on-write)")
+            self.pending_copies.append((last.block_id, copy.block_id))
+            self.pool.free(last)
+            st.blocks[idx] = copy
+            last = copy
+        slot = last.block_id * bs + st.num_tokens % bs
         st.num_tokens += 1
+        if st.token_ids is not None:
+            st.token_ids.append(-1 if token_id is None else int(token_id))
+            if st.num_tokens % bs == 0:
+                parent = 0 if idx == 0 else st.blocks[idx - 1].block_hash
+                if parent is not None:
+                    self.pool.cache(last, hash_block_tokens(
+                        parent, st.token_ids[idx * bs:(idx + 1) * bs]))
         return slot
 
     def free_seq(self, seq_id: int) -> None:

@@ -22,15 +22,18 @@ head size x dtype bytes; "vLLM innenfra", KV-cache-manager paragraph), not
 the order of the axes inside it; the order above is this library's choice.
 
 Recipe (one ``numpy.random.SeedSequence(seed)``, children drawn in a fixed
-order: lengths, free-queue permutation, q, K pool, V pool, k_new, v_new):
+order: lengths, free-queue permutation, q, K pool, V pool, k_new, v_new;
+an eighth child draws the token ids of the prefix case):
 
 * lengths: integers, ``uniform[a, b]`` inclusive, or lognormal rounded and
   clipped, or the fixed list of the tiny case;
 * the free queue starts as a random permutation of all physical blocks, so
   consecutive logical blocks land on unrelated physical blocks;
 * every sequence is admitted with ``seq_len - 1`` cached tokens (the prefix
-  case: ``2048 + suffix``), then one token is appended through the pool's
-  allocate-on-growth rule, which yields ``slot_mapping``;
+  case: ``2048 + suffix``, with a shared prompt's token ids, so that the
+  block manager's hash-keyed prefix cache maps every later sequence's first
+  128 blocks to the first sequence's), then one token is appended through
+  the pool's allocate-on-growth rule, which yields ``slot_mapping``;
 * q, K, V, k_new, v_new ~ N(0, 1) drawn in float32, then rounded to the
   storage dtype (bf16: round-to-nearest-even; fp8 e4m3fn: divided by a
   per-tensor scale ``amax/448``, clamped to +-448, rounded to nearest even);
@@ -240,10 +243,18 @@ def build_case(cfg: DecodeConfig, seed: int = 0) -> DecodeCase:
     if cfg.lens == "prefix":
         if cfg.prefix_len % BLOCK_SIZE:
             raise ValueError("shared prefix must be whole blocks")
-        assert mgr.admit(0, int(existing[0]))
-        shared = mgr.req_to_blocks[0].blocks[:cfg.prefix_len // BLOCK_SIZE]
-        for i in range(1, b):
-            assert mgr.admit(i, int(existing[i]), shared_prefix=shared)
+        # token ids: one shared prompt prefix, then per-sequence tokens; the
+        # block manager's hash cache finds the prefix blocks for every
+        # sequence after the first
+        rng_tok = np.random.default_rng(
+            np.random.SeedSequence(seed).spawn(8)[7])
+        prefix_ids = rng_tok.integers(0, 1 << 17, size=cfg.prefix_len)
+        for i in range(b):
+            own = rng_tok.integers(0, 1 << 17,
+                                   size=int(existing[i]) - cfg.prefix_len)
+            ok, hits = mgr.admit_cached(i, np.concatenate([prefix_ids, own]))
+            assert ok and hits == (0 if i == 0 else
+                                   cfg.prefix_len // BLOCK_SIZE)
     else:
         for i in range(b):
             assert mgr.admit(i, int(existing[i]))

@@ -51,6 +51,7 @@ def test_struct_layout_matches_the_header():
     fields = {
         "pa_decode_desc": _lib.DecodeDesc,
         "pa_append_desc": _lib.AppendDesc,
+        "pa_copy_desc": _lib.CopyDesc,
     }
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "pa.h"',
              "int main(void) {"]
@@ -169,6 +170,24 @@ def test_quantising_append_checks(lib):
     a.kv_dtype, a.num_tokens = _lib.PA_FP8_E4M3FN, 0
     assert q(None, None, None, None, None, ctypes.byref(a), one, one,
              None) == 0
+
+
+def test_copy_blocks_checks(lib):
+    p, odd = ctypes.c_void_p(256), ctypes.c_void_p(258)
+    c = _lib.CopyDesc(num_pairs=2, num_kv_heads=8, head_size=128,
+                      block_size=16, num_blocks=10, kv_dtype=_lib.PA_BF16)
+    f = lib.pa_copy_blocks
+    assert f(None, p, p, p, ctypes.byref(c), None) == -1
+    assert f(p, p, p, None, ctypes.byref(c), None) == -1
+    assert f(odd, p, p, p, ctypes.byref(c), None) == -4
+    assert f(p, p, ctypes.c_void_p(257), p, ctypes.byref(c), None) == -4
+    c.head_size = 96
+    assert f(p, p, p, p, ctypes.byref(c), None) == -3
+    c.head_size, c.kv_dtype = 128, 9
+    assert f(p, p, p, p, ctypes.byref(c), None) == -2
+    c.kv_dtype, c.num_pairs = _lib.PA_BF16, 0
+    assert f(None, None, None, None, ctypes.byref(c), None) == 0
+    assert f(p, p, p, p, None, None) == -1
 
 
 def test_empty_calls_are_no_ops(lib):

@@ -76,16 +76,88 @@ def test_shared_prefix_ref_counts_and_copy_on_write_guard():
     assert [b.ref_cnt for b in shared] == [1, 1]
 
 
-def test_append_into_shared_block_raises():
+def test_append_into_shared_block_copies_it_first():
+    """Copy-on-write: a fork shares the partly filled last block; the first
+    append of either sequence takes a copy for the writer."""
     pool = BlockPool(8)
     mgr = KVCacheManager(pool, 16)
-    assert mgr.admit(0, 16)
-    blk = mgr.req_to_blocks[0].blocks[0]
-    # a second request shares the (full) block and then holds 10 tokens of it
-    assert mgr.admit(1, 16, shared_prefix=[blk])
-    mgr.req_to_blocks[1].num_tokens = 10
-    with pytest.raises(RuntimeError):
-        mgr.append_slot(1)
+    assert mgr.admit(0, 20)                   # blocks: full + 4 tokens
+    a, b = mgr.req_to_blocks[0].blocks
+    mgr.fork(0, 1)
+    assert (a.ref_cnt, b.ref_cnt) == (2, 2)
+    slot = mgr.append_slot(1)                 # the fork writes first
+    (src, dst), = mgr.take_copies()
+    assert src == b.block_id and dst != b.block_id
+    assert slot == dst * 16 + 4
+    assert mgr.block_ids(1) == [a.block_id, dst]
+    assert mgr.block_ids(0) == [a.block_id, b.block_id]
+    assert (a.ref_cnt, b.ref_cnt) == (2, 1)
+    # the original now owns its block alone: no copy
+    assert mgr.append_slot(0) == b.block_id * 16 + 4
+    assert mgr.take_copies() == []
+    mgr.free_seq(1)
+    mgr.free_seq(0)
+    assert pool.num_free == 8
+
+
+def test_prefix_cache_hits_full_blocks_only():
+    pool = BlockPool(16)
+    mgr = KVCacheManager(pool, 16)
+    prompt = list(range(100, 140))            # 2 full blocks + 8 tokens
+    ok, hits = mgr.admit_cached(0, prompt)
+    assert ok and hits == 0
+    ok, hits = mgr.admit_cached(1, prompt[:36] + [7, 7, 7, 7])
+    assert ok and hits == 2
+    b0, b1 = mgr.block_ids(0), mgr.block_ids(1)
+    assert b1[:2] == b0[:2] and b1[2] != b0[2]
+    assert [blk.ref_cnt for blk in mgr.req_to_blocks[0].blocks] == [2, 2, 1]
+    # a change inside block 1 keeps only block 0 (hashes are chained)
+    other = list(prompt)
+    other[20] = -5
+    ok, hits = mgr.admit_cached(2, other)
+    assert ok and hits == 1
+    # the same tokens under another parent do not hit
+    ok, hits = mgr.admit_cached(3, [0] * 16 + prompt[16:32])
+    assert ok and hits == 0
+
+
+def test_prefix_cache_survives_free_until_evicted():
+    pool = BlockPool(4, order=range(4))
+    mgr = KVCacheManager(pool, 16)
+    prompt = list(range(32))
+    assert mgr.admit_cached(0, prompt) == (True, 0)
+    ids = mgr.block_ids(0)
+    mgr.free_seq(0)                           # both blocks free but cached
+    assert pool.num_free == 4
+    assert mgr.admit_cached(1, prompt) == (True, 2)
+    assert mgr.block_ids(1) == ids and pool.num_free == 2
+    mgr.free_seq(1)
+    # allocation pressure pops the cached blocks and evicts them
+    assert mgr.admit(2, 64)
+    assert pool.cached_block_hash_to_block == {}
+    mgr.free_seq(2)
+    assert mgr.admit_cached(3, prompt) == (True, 0)
+
+
+def test_prefix_cache_registers_blocks_filled_by_appends():
+    pool = BlockPool(8)
+    mgr = KVCacheManager(pool, 16)
+    assert mgr.admit_cached(0, list(range(10))) == (True, 0)
+    for t in range(10, 16):
+        mgr.append_slot(0, token_id=t)
+    assert mgr.admit_cached(1, list(range(16)) + [99]) == (True, 1)
+    assert mgr.block_ids(1)[0] == mgr.block_ids(0)[0]
+
+
+def test_prefix_cache_hits_in_the_free_queue_are_not_double_booked():
+    pool = BlockPool(3, order=range(3))
+    mgr = KVCacheManager(pool, 16)
+    assert mgr.admit_cached(0, list(range(32))) == (True, 0)
+    mgr.free_seq(0)
+    # 2 cached hits (free) + 2 fresh blocks > 3 blocks: refused, unchanged
+    assert mgr.admit_cached(1, list(range(32)) + [1] * 20) == (False, 0)
+    assert pool.num_free == 3 and len(pool.cached_block_hash_to_block) == 2
+    assert mgr.admit_cached(1, list(range(32)) + [1] * 10) == (True, 2)
 
 
 def test_fcfs_admission_reproduces_capacity_example():
