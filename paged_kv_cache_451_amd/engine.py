@@ -1,0 +1,340 @@
+"""A synthetic continuous-batching engine loop over the paged KV cache.
+
+The pages describe the serving loop around the paged cache ("vLLM innenfra",
+the ``step()`` paragraphs; "PagedAttention：KV cache 即虚拟内存（block manager
+& 碎片）", section "深入原理", lifecycle bullet):
+
+* each ``step()`` schedules work, runs the forward pass and post-processes:
+  finished requests hand their blocks back to the free-block queue;
+* new requests join between steps (continuous batching), first come first
+  served; when the pool is full the scheduler queues them;
+* a request's prompt takes its blocks on admission, decoding takes one more
+  block whenever the last one is full;
+* under pool pressure a running request is preempted (evicted and later
+  recomputed, like a page-out) so that the others can keep growing.
+
+There is no model here: random K/V stand in for the projections of each
+token and random queries for the attention input, so the loop exercises the
+block manager and the device path (``pa_kv_append`` for prompt tokens,
+``pa_decode_append`` for one new token per running request) at the scale of
+a serving batch.  ``contiguous_capacity`` gives the number of requests a
+cache that reserves ``max_len`` tokens per request would hold in the same
+pool, for comparison with the concurrency the paged cache reaches.
+
+Readings where the pages leave a step open:
+
+* a preempted request is the most recently admitted running one; its blocks
+  are freed and it goes back to the front of the waiting queue; on
+  re-admission its prompt and the tokens generated so far are written again
+  (recompute);
+* admission is first come first served and stops at the first waiting
+  request whose tokens do not fit next to the blocks the running requests
+  need for this step's new tokens;
+* every running request decodes one token per step; a request finishes
+  after ``max_new_tokens`` decoded tokens and frees its blocks in the same
+  step.
+"""
+from __future__ import annotations
+
+import math
+from collections import deque
+from dataclasses import dataclass, field
+from typing import Deque, Dict, List, Optional
+
+import numpy as np
+
+from .pool import BlockPool, KVCacheManager
+
+BLOCK_SIZE = 16
+
+
+@dataclass
+class Request:
+    req_id: int
+    prompt_ids: List[int]
+    max_new_tokens: int
+    output_ids: List[int] = field(default_factory=list)
+    admitted_step: int = -1
+    finished_step: int = -1
+    preemptions: int = 0
+
+    @property
+    def num_tokens(self) -> int:
+        return len(self.prompt_ids) + len(self.output_ids)
+
+    @property
+    def done(self) -> bool:
+        return len(self.output_ids) >= self.max_new_tokens
+
+
+@dataclass
+class StepStats:
+    step: int
+    running: int                 # requests that decoded a token this step
+    waiting: int
+    admitted: int
+    preempted: int
+    finished: int
+    prefill_tokens: int          # prompt tokens written this step
+    cached_prefix_tokens: int    # prompt tokens found in the prefix cache
+    blocks_used: int
+    slots_used: int              # tokens stored in the cache
+
+
+def contiguous_capacity(num_blocks: int, max_len: int,
+                        block: int = BLOCK_SIZE) -> int:
+    """Requests a cache reserving max_len tokens per request can hold."""
+    return num_blocks // math.ceil(max_len / block)
+
+
+class Engine:
+    """Continuous batching over a paged KV pool on one GPU.
+
+    ``device=None`` runs the scheduler and block manager only (no kernels),
+    for host-side tests.  ``mirror=True`` keeps a host copy of every K/V
+    value written (and the step's queries) so that each decode can be
+    checked against the oracle.
+    """
+
+    def __init__(self, num_blocks: int, num_q_heads: int, num_kv_heads: int,
+                 head_size: int, *, device=None, seed: int = 0,
+                 max_running: Optional[int] = None,
+                 prefix_caching: bool = True, mirror: bool = False):
+        self.num_blocks = num_blocks
+        self.hq, self.hkv, self.d = num_q_heads, num_kv_heads, head_size
+        rng = np.random.default_rng(seed)
+        self.rng = rng
+        self.pool = BlockPool(num_blocks, order=rng.permutation(num_blocks))
+        self.mgr = KVCacheManager(self.pool, BLOCK_SIZE)
+        self.max_running = max_running
+        self.prefix_caching = prefix_caching
+        self.waiting: Deque[Request] = deque()
+        self.running: List[Request] = []        # in admission order
+        self.finished: List[Request] = []
+        self.step_no = 0
+        self.device = device
+        self.mirror = mirror
+        self.scale = float(np.float32(1.0 / math.sqrt(head_size)))
+        self.last_out = None
+        self.last_batch: List[int] = []
+        self._dev_rand: Dict[str, object] = {}
+        # (start event, end event, KV bytes) of each decode, when timed
+        self.time_decode = False
+        self.decode_events: List[tuple] = []
+        if device is not None:
+            import torch
+            self.torch = torch
+            self.k_pool = torch.zeros(num_blocks, num_kv_heads, BLOCK_SIZE,
+                                      head_size, dtype=torch.bfloat16,
+                                      device=device)
+            self.v_pool = torch.zeros(num_blocks, num_kv_heads, head_size,
+                                      BLOCK_SIZE, dtype=torch.bfloat16,
+                                      device=device)
+        if mirror:
+            self.k_host = np.zeros((num_blocks, num_kv_heads, BLOCK_SIZE,
+                                    head_size), dtype=np.uint16)
+            self.v_host = np.zeros((num_blocks, num_kv_heads, head_size,
+                                    BLOCK_SIZE), dtype=np.uint16)
+            self.last_q = None
+
+    # -- requests ------------------------------------------------------------
+    def add_request(self, req: Request) -> None:
+        self.waiting.append(req)
+
+    def has_work(self) -> bool:
+        return bool(self.waiting or self.running)
+
+    # -- scheduling ------------------------------------------------------------
+    def _preempt_last(self) -> Request:
+        victim = self.running.pop()
+        self.mgr.free_seq(victim.req_id)
+        victim.preemptions += 1
+        self.waiting.appendleft(victim)
+        return victim
+
+    def _growth_need(self) -> int:
+        """Blocks the running requests take for this step's new tokens."""
+        return sum(1 for r in self.running
+                   if self.mgr.req_to_blocks[r.req_id].num_tokens %
+                   BLOCK_SIZE == 0)
+
+    def _ensure_growth(self) -> int:
+        """Every running request needs a slot for its next token; preempt
+        from the back until the blocks needed fit in the pool."""
+        preempted = 0
+        while self.running and self._growth_need() > self.pool.num_free:
+            self._preempt_last()
+            preempted += 1
+        return preempted
+
+    def _admit(self) -> List[tuple]:
+        """FCFS admission; returns (request, cached prompt tokens) pairs."""
+        admitted = []
+        while self.waiting:
+            if self.max_running is not None and \
+                    len(self.running) >= self.max_running:
+                break
+            req = self.waiting[0]
+            ids = req.prompt_ids + req.output_ids
+            if self.prefix_caching:
+                ok, hits = self.mgr.admit_cached(req.req_id, ids)
+            else:
+                ok, hits = self.mgr.admit(req.req_id, len(ids)), 0
+            if not ok:
+                break
+            self.running.append(req)
+            if self._growth_need() > self.pool.num_free:
+                # its first decoded token (or another request's) would not
+                # fit: undo and keep it waiting
+                self.running.pop()
+                self.mgr.free_seq(req.req_id)
+                break
+            self.waiting.popleft()
+            if req.admitted_step < 0:
+                req.admitted_step = self.step_no
+            admitted.append((req, hits * BLOCK_SIZE))
+        return admitted
+
+    # -- device work -------------------------------------------------------------
+    def _random_rows(self, n: int):
+        """n random K and V rows (bf16).  With a mirror they are drawn on the
+        host, seeded; otherwise they are slices of a random device buffer
+        (their values do not matter to the loop)."""
+        import torch
+        if not self.mirror and self.device is not None:
+            return self._device_rows(n, "kv")
+        g = torch.Generator().manual_seed(int(self.rng.integers(1 << 62)))
+        k = torch.randn(n, self.hkv, self.d, generator=g).to(torch.bfloat16)
+        v = torch.randn(n, self.hkv, self.d, generator=g).to(torch.bfloat16)
+        return k, v
+
+    def _device_rows(self, n: int, what: str):
+        import torch
+        heads = self.hq if what == "q" else self.hkv
+        buf = self._dev_rand.get(what)
+        if buf is None or buf.shape[0] < 2 * n:
+            rows = max(2 * n, 4096)
+            buf = torch.randn(rows, heads, self.d, device=self.device).to(
+                torch.bfloat16)
+            self._dev_rand[what] = buf
+        if what == "q":
+            return buf[:n]
+        return buf[:n], buf[n:2 * n]
+
+    def _write_prompts(self, admitted) -> int:
+        slots = []
+        for req, cached in admitted:
+            blocks = self.mgr.block_ids(req.req_id)
+            n = req.num_tokens
+            slots += [blocks[t // BLOCK_SIZE] * BLOCK_SIZE + t % BLOCK_SIZE
+                      for t in range(cached, n)]
+        if not slots:
+            return 0
+        if self.device is None and not self.mirror:
+            return len(slots)
+        k, v = self._random_rows(len(slots))
+        slots_np = np.asarray(slots, dtype=np.int32)
+        if self.mirror:
+            self._mirror_write(k, v, slots)
+        if self.device is not None:
+            from . import _lib
+            t = self.torch
+            _lib.pa_kv_append(k.to(self.device), v.to(self.device),
+                              t.from_numpy(slots_np).to(self.device),
+                              self.k_pool, self.v_pool)
+        return len(slots)
+
+    def step(self) -> StepStats:
+        preempted = self._ensure_growth()
+        admitted = self._admit()
+        if not self.running and self.waiting:
+            req = self.waiting[0]
+            raise MemoryError(
+                f"request {req.req_id} ({req.num_tokens} tokens) does not fit "
+                f"in an empty pool of {self.num_blocks} blocks")
+        prefill = self._write_prompts(admitted)
+        cached = sum(c for _, c in admitted)
+        batch = list(self.running)
+        finished = 0
+        if batch:
+            slots = [self.mgr.append_slot(r.req_id,
+                                          token_id=int(self.rng.integers(
+                                              1 << 17)))
+                     for r in batch]
+            copies = self.mgr.take_copies()
+            assert not copies, "running requests never share a partial block"
+            self._decode(batch, slots)
+            for r, s in zip(batch, slots):
+                tok = self.mgr.req_to_blocks[r.req_id].token_ids
+                r.output_ids.append(tok[-1] if tok else 0)
+            still = []
+            for r in self.running:
+                if r.done:
+                    self.mgr.free_seq(r.req_id)
+                    r.finished_step = self.step_no
+                    self.finished.append(r)
+                    finished += 1
+                else:
+                    still.append(r)
+            self.running = still
+        st = StepStats(
+            step=self.step_no, running=len(batch), waiting=len(self.waiting),
+            admitted=len(admitted), preempted=preempted, finished=finished,
+            prefill_tokens=prefill, cached_prefix_tokens=cached,
+            blocks_used=self.num_blocks - self.pool.num_free,
+            slots_used=sum(self.mgr.req_to_blocks[r.req_id].num_tokens
+                           for r in self.running))
+        self.step_no += 1
+        return st
+
+    def _decode(self, batch, slots) -> None:
+        self.last_batch = [r.req_id for r in batch]
+        if self.device is None and not self.mirror:
+            return
+        import torch
+        ids = [r.req_id for r in batch]
+        tables, lens = self.mgr.tables(ids)
+        n = len(batch)
+        if self.mirror or self.device is None:
+            g = torch.Generator().manual_seed(int(self.rng.integers(1 << 62)))
+            q = torch.randn(n, self.hq, self.d, generator=g).to(
+                torch.bfloat16)
+        else:
+            q = self._device_rows(n, "q")
+        kn, vn = self._random_rows(n)
+        if self.mirror:
+            self._mirror_write(kn, vn, slots)
+            self.last_q = q
+            self.last_tables, self.last_lens = tables, lens
+        if self.device is None:
+            return
+        from . import _lib
+        dev = self.device
+        out = torch.empty(n, self.hq, self.d, dtype=torch.bfloat16,
+                          device=dev)
+        if self.time_decode:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        _lib.pa_decode_append(
+            q.to(dev), self.k_pool, self.v_pool,
+            torch.from_numpy(tables).to(dev),
+            torch.from_numpy(lens.astype(np.int32)).to(dev), self.scale, out,
+            kn.to(dev), vn.to(dev),
+            torch.from_numpy(np.asarray(slots, dtype=np.int32)).to(dev),
+            max_seq_len=int(lens.max()),
+            total_blocks_hint=int(((lens + 15) // 16).sum()))
+        if self.time_decode:
+            e1.record()
+            self.decode_events.append(
+                (e0, e1, int(lens.sum()) * self.hkv * self.d * 2 * 2))
+        self.last_out = out
+
+    def _mirror_write(self, k, v, slots) -> None:
+        import torch
+        kb = k.view(torch.uint16).numpy()
+        vb = v.view(torch.uint16).numpy()
+        for i, s in enumerate(slots):
+            p, o = divmod(int(s), BLOCK_SIZE)
+            self.k_host[p, :, o, :] = kb[i]
+            self.v_host[p, :, :, o] = vb[i]
