@@ -51,13 +51,14 @@ def parse():
                         "then pa_decode) instead of pa_decode_append")
     p.add_argument("--op", default="step",
                    choices=["step", "append", "append_quant",
-                            "copy_blocks", "engine"],
+                            "copy_blocks", "engine", "prefill"],
                    help="step: the decode step (default); append / "
                         "append_quant: writing --tokens new tokens into a "
                         "pool (bf16 copy, or bf16 -> fp8 e4m3fn "
                         "quantisation); copy_blocks: copy-on-write of "
                         "--pairs whole blocks; engine: the synthetic "
-                        "continuous-batching loop")
+                        "continuous-batching loop; prefill: chunked-prefill "
+                        "attention (--config prefill_llama3_8b_bf16)")
     p.add_argument("--pairs", type=int, default=4096,
                    help="block pairs copied per launch by --op copy_blocks")
     p.add_argument("--tokens", type=int, default=32768,
@@ -301,6 +302,107 @@ def bench_copy_blocks(a, torch, _lib):
     }), flush=True)
 
 
+def _causal_pairs(seq_lens, q_start) -> int:
+    """(query, attended key) pairs of a chunked prefill: query i of a
+    C-token chunk over L cached tokens attends to L - C + i + 1 keys."""
+    total = 0
+    for b, n in enumerate(seq_lens):
+        c = int(q_start[b + 1] - q_start[b])
+        total += c * (n - c + 1) + c * (c - 1) // 2
+    return total
+
+
+def bench_prefill(a, torch, _lib):
+    """Chunked-prefill attention over the paged pool: every sequence's chunk
+    of query tokens against its cached context, causal within the chunk.
+    The algorithmic work is 4 * D * Hq flops per (query, attended key) pair
+    (the QK^T and PV multiply-adds); the kernel also computes the masked
+    half of the 32-key steps that cross the diagonal, which is not
+    counted."""
+    from paged_kv_cache_451_amd.workloads import PREFILL_BY_NAME, \
+        build_prefill_case
+
+    name = a.config if a.config in PREFILL_BY_NAME else \
+        "prefill_llama3_8b_bf16"
+    cfg = PREFILL_BY_NAME[name]
+    case = build_prefill_case(cfg, seed=a.seed or 0)
+    dev = {k: getattr(case, k).cuda() for k in
+           ("q", "k_pool", "v_pool", "block_tables", "seq_lens", "q_start")}
+    out = torch.empty_like(dev["q"])
+    desc = _lib.prefill_desc(dev["q"], dev["k_pool"], dev["block_tables"],
+                             cfg.num_seqs)
+
+    def call():
+        _lib.pa_prefill(dev["q"], dev["k_pool"], dev["v_pool"],
+                        dev["block_tables"], dev["seq_lens"], dev["q_start"],
+                        case.scale, out, desc)
+
+    for _ in range(a.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = _kernel_events(torch, a.steps)
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / a.steps
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    avg = sum(ms) / len(ms)
+    lens = case.seq_lens.tolist()
+    qs = case.q_start.tolist()
+    pairs = _causal_pairs(lens, qs)
+    flops = 4 * cfg.head_size * cfg.num_q_heads * pairs
+    tflops = flops / (avg * 1e-3) / 1e12
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        from oracle.adapters import prefill_args
+        args = prefill_args(case)
+        done, t_cpu, cpu_pairs = 0, 0.0, 0
+        while t_cpu < a.cpu_seconds:
+            b = done % cfg.num_seqs
+            args["seqs"] = [b]
+            t1 = time.perf_counter()
+            oracle.paged_prefill(**args)
+            t_cpu += time.perf_counter() - t1
+            cpu_pairs += _causal_pairs([lens[b]], [0, qs[b + 1] - qs[b]])
+            done += 1
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()]
+                      or [1])
+        cpu = {"value": round(4 * cfg.head_size * cfg.num_q_heads * cpu_pairs
+                              / t_cpu / 1e12, 6),
+               "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"float64 numpy oracle, {done} whole chunks taken in "
+                         f"order from the {cfg.num_seqs} sequences of this "
+                         f"workload ({t_cpu:.1f} s)"}
+    print(json.dumps({
+        "metric": "chunked-prefill attention over the paged pool: TFLOP/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(avg, 5),
+        "wall_ms_per_step": round(wall * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "num_seqs": cfg.num_seqs,
+                   "chunk": cfg.chunk, "prior_tokens": [cfg.prior_lo,
+                                                        cfg.prior_hi],
+                   "num_q_heads": cfg.num_q_heads,
+                   "num_kv_heads": cfg.num_kv_heads,
+                   "head_size": cfg.head_size, "query_tokens": qs[-1],
+                   "context_tokens": int(sum(lens))},
+        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel",
+                     "achieved": round(tflops, 2), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": flops,
+                     "kernel_ms_avg": round(avg, 5),
+                     "kernel_ms_median": round(ms[len(ms) // 2], 5)},
+        "cpu_baseline": cpu,
+    }), flush=True)
+
+
 def bench_engine(a, torch):
     """The synthetic continuous-batching loop on the Llama-3-8B shape
     (32 q / 8 KV heads, head size 128, bf16) with a 16384-block pool:
@@ -398,6 +500,9 @@ def main():
         return
     if a.op == "engine":
         bench_engine(a, torch)
+        return
+    if a.op == "prefill":
+        bench_prefill(a, torch, _lib)
         return
     if a.op != "step":
         bench_append(a, torch, _lib)

@@ -285,6 +285,61 @@ int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_blocks,
                    const int32_t* dst_blocks, const pa_copy_desc* desc,
                    void* stream);
 
+/*
+ * Shapes of one chunked-prefill call.
+ *   num_seqs            B >= 0 (at most 65536)
+ *   num_q_heads         Hq, a multiple of num_kv_heads, Hq/Hkv <= 16
+ *   num_kv_heads        Hkv >= 1
+ *   head_size           D in {64, 128}
+ *   block_size          must be 16
+ *   num_blocks          NB >= 1
+ *   max_blocks_per_seq  row length of block_tables
+ *   num_query_tokens    T = q_start[B], the packed query rows of q / out
+ *   q_dtype, kv_dtype   both PA_BF16
+ */
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_size;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t num_query_tokens;
+  pa_dtype q_dtype;
+  pa_dtype kv_dtype;
+} pa_prefill_desc;
+
+/*
+ * Chunked-prefill attention over the paged pool.  A prompt may be cut into
+ * chunks that the scheduler mixes with decode work ("vLLM innenfra",
+ * step() and continuous-batching paragraphs); the chunk's own K/V are in
+ * the pool already (pa_kv_append), and each of its query tokens attends to
+ * every cached token before it and to the chunk up to itself.  For
+ * sequence b with L = seq_lens[b] cached tokens and chunk rows
+ * q_start[b] .. q_start[b+1] (C rows), query row i sits at position
+ * p = L - C + i and
+ *     out[q_start[b] + i][h][:] = sum_{t <= p} softmax_t(scale <q, K_t>) V_t
+ * with K_t, V_t of KV head h / (Hq / Hkv) found through the block table.
+ * The result equals dense causal attention over the contiguous context
+ * ("PagedAttention：KV cache 即虚拟内存", section "直接答案").
+ *   q, out          [T][Hq][D] bf16, 16-byte aligned
+ *   k_pool, v_pool  as for pa_decode (bf16)
+ *   block_tables    int32 [B][max_blocks_per_seq]
+ *   seq_lens        int32 [B], the chunk included
+ *   q_start         int32 [B+1], non-decreasing, q_start[B] = T
+ * Containment: q_start values are clamped to [0, T] (rows outside are not
+ * read or written), seq_lens to [0, max_blocks_per_seq * 16]; a chunk
+ * longer than its sequence gives zero rows for tokens before position 0;
+ * block ids outside [0, NB) contribute nothing.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_ALIGN,
+ * PA_ERR_LAUNCH.  Asynchronous on `stream`; no workspace.
+ */
+int pa_prefill(const void* q, const void* k_pool, const void* v_pool,
+               const int32_t* block_tables, const int32_t* seq_lens,
+               const int32_t* q_start, float scale, void* out,
+               const pa_prefill_desc* desc, void* stream);
+
 /* Static English text of a pa_status value. */
 const char* pa_status_string(int status);
 

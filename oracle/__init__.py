@@ -17,11 +17,15 @@ Modules:
   capacity example.
 * ``quant``    - the quantising append into an fp8 e4m3fn pool (nearest
   e4m3fn value of x / scale, saturating, ties to even).
+* ``prefill``  - chunked-prefill attention: each chunk token attends to the
+  cached tokens before it and to the chunk up to itself.
 
-Every function is pinned by ``tests/test_oracle.py`` and
-``tests/test_quant.py`` against library routines, closed forms, invariants,
-brute force and the pages' printed example; none is "parity unpinned".
+Every function is pinned by ``tests/test_oracle.py``,
+``tests/test_quant.py`` and ``tests/test_prefill_oracle.py`` against
+library routines, closed forms, invariants, brute force and the pages'
+printed example; none is "parity unpinned".
 """
-from . import append, capacity, decode, numerics, quant  # noqa: F401
+from . import append, capacity, decode, numerics, prefill, quant  # noqa: F401
 from .append import kv_append  # noqa: F401
 from .decode import paged_decode, attention_weights  # noqa: F401
+from .prefill import paged_prefill, prefill_flops  # noqa: F401

@@ -46,3 +46,15 @@ def appended_pools(case):
     kn, _ = raw(case.k_new)
     vn, _ = raw(case.v_new)
     return kv_append(k, v, kn, vn, case.slot_mapping.numpy())
+
+
+def prefill_args(case, seqs=None):
+    """Keyword arguments of ``paged_prefill`` for a generated prefill case."""
+    q, q_dtype = raw(case.q)
+    k, kv_dtype = raw(case.k_pool)
+    v, _ = raw(case.v_pool)
+    return dict(q=q, k_raw=k, v_raw=v,
+                block_tables=case.block_tables.numpy(),
+                seq_lens=case.seq_lens.numpy(),
+                q_start=case.q_start.numpy(), scale=case.scale,
+                q_dtype=q_dtype, kv_dtype=kv_dtype, seqs=seqs)

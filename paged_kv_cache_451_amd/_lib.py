@@ -26,8 +26,8 @@ _DTYPE = {
 # names every build of the library exports (checked by the tests)
 EXPORTS = ("pa_decode", "pa_decode_workspace_size", "pa_decode_append",
            "pa_decode_append_workspace_size", "pa_kv_append",
-           "pa_kv_append_quant", "pa_copy_blocks", "pa_status_string",
-           "pa_abi_version")
+           "pa_kv_append_quant", "pa_copy_blocks", "pa_prefill",
+           "pa_status_string", "pa_abi_version")
 
 
 class DecodeDesc(ctypes.Structure):
@@ -73,6 +73,21 @@ class CopyDesc(ctypes.Structure):
     ]
 
 
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_query_tokens", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int),
+        ("kv_dtype", ctypes.c_int),
+    ]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -109,6 +124,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, ctypes.POINTER(CopyDesc),
                                    vp]
     lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                               ctypes.POINTER(PrefillDesc), vp]
+    lib.pa_prefill.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_abi_version.argtypes = []
@@ -262,6 +280,29 @@ def pa_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks) -> None:
     _check(lib.pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(src_blocks),
                               _ptr(dst_blocks), ctypes.byref(desc),
                               _stream()))
+
+
+def prefill_desc(q, k_pool, block_tables, num_seqs: int) -> PrefillDesc:
+    t, hq, d = q.shape
+    nb, hkv, bs, _ = k_pool.shape
+    return PrefillDesc(num_seqs=num_seqs, num_q_heads=hq, num_kv_heads=hkv,
+                       head_size=d, block_size=bs, num_blocks=nb,
+                       max_blocks_per_seq=block_tables.shape[1],
+                       num_query_tokens=t, q_dtype=_DTYPE[q.dtype],
+                       kv_dtype=_DTYPE[k_pool.dtype])
+
+
+def pa_prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, scale,
+               out, desc: Optional[PrefillDesc] = None) -> torch.Tensor:
+    """Chunked-prefill attention into ``out`` (see ``include/pa.h``)."""
+    lib = load()
+    if desc is None:
+        desc = prefill_desc(q, k_pool, block_tables, seq_lens.numel())
+    _check(lib.pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool),
+                          _ptr(block_tables), _ptr(seq_lens), _ptr(q_start),
+                          ctypes.c_float(scale), _ptr(out),
+                          ctypes.byref(desc), _stream()))
+    return out
 
 
 class PreparedStep:

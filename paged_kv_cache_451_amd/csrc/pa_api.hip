@@ -366,4 +366,59 @@ int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_blocks,
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+int pa_prefill(const void* q, const void* k_pool, const void* v_pool,
+               const int32_t* block_tables, const int32_t* seq_lens,
+               const int32_t* q_start, float scale, void* out,
+               const pa_prefill_desc* desc, void* stream) {
+  if (!desc) return PA_ERR_NULL;
+  const pa_prefill_desc* d = desc;
+  if (d->num_seqs < 0 || d->num_seqs > 65536 || d->num_query_tokens < 0)
+    return PA_ERR_SHAPE;
+  if (d->num_kv_heads < 1 || d->num_q_heads < d->num_kv_heads ||
+      d->num_q_heads % d->num_kv_heads ||
+      d->num_q_heads / d->num_kv_heads > 16)
+    return PA_ERR_SHAPE;
+  if ((d->head_size != 64 && d->head_size != 128) ||
+      d->block_size != pa::kBlock)
+    return PA_ERR_SHAPE;
+  if (d->num_blocks < 1 || (int64_t)d->num_blocks * pa::kBlock > INT32_MAX ||
+      d->max_blocks_per_seq < 1 ||
+      (int64_t)d->max_blocks_per_seq * pa::kBlock > INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (d->q_dtype != PA_BF16 || d->kv_dtype != PA_BF16) return PA_ERR_DTYPE;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if ((int64_t)d->num_query_tokens * d->num_q_heads > INT32_MAX ||
+      pa::prefill_grid(d->head_size, d->num_query_tokens, G, d->num_seqs,
+                       d->num_kv_heads) > INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (d->num_seqs == 0 || d->num_query_tokens == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !q_start ||
+      !out)
+    return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned16(out) || ((uintptr_t)block_tables & 3u) ||
+      ((uintptr_t)seq_lens & 3u) || ((uintptr_t)q_start & 3u))
+    return PA_ERR_ALIGN;
+  pa::PrefillArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.q_start = q_start;
+  a.out = out;
+  a.s.B = d->num_seqs;
+  a.s.Hq = d->num_q_heads;
+  a.s.Hkv = d->num_kv_heads;
+  a.s.G = G;
+  a.s.max_blocks = d->max_blocks_per_seq;
+  a.s.NB = d->num_blocks;
+  a.s.T = d->num_query_tokens;
+  a.s.c_log2 = (float)((double)scale * 1.4426950408889634);
+  hipError_t e =
+      pa::launch_prefill(d->head_size, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 }  // extern "C"

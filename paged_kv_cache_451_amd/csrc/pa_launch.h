@@ -74,6 +74,32 @@ hipError_t launch_kv_append_quant(const void* k_new, const void* v_new,
                                   int num_blocks, float k_scale,
                                   float v_scale, hipStream_t stream);
 
+// Chunked prefill (prefill_mfma.hip): query row tiles of
+// 4 waves * 16 * kPrefillTiles rows per workgroup.
+constexpr int kPrefillTiles = 2;
+struct PrefillSched {
+  int B;           // sequences
+  int Hq, Hkv, G;  // heads
+  int max_blocks;  // row length of block_tables
+  int NB;          // pool blocks
+  int T;           // packed query rows (q_start[B])
+  float c_log2;    // scale * log2(e)
+};
+struct PrefillArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* q_start;
+  void* out;
+  PrefillSched s;
+};
+// Workgroups the prefill launch uses (an upper bound on the query tiles).
+int64_t prefill_grid(int head_size, int64_t T, int G, int B, int Hkv);
+hipError_t launch_prefill(int head_size, const PrefillArgs& a,
+                          hipStream_t stream);
+
 // Copy-on-write block copy: K and V block src[i] -> dst[i] for every pair
 // (block_bytes per pool block, a multiple of 16).  Pairs with an id outside
 // [0, num_blocks) are skipped.

@@ -349,3 +349,100 @@ def algorithmic_bytes(case: DecodeCase) -> dict:
             "main_fused": main_fused,
             "append": append, "step": decode + append,
             "context_tokens": int(lens.sum())}
+
+
+# --------------------------------------------------------------------------
+# chunked prefill: a chunk of query tokens per sequence over the paged pool
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_size: int
+    chunk: int                     # query tokens per sequence
+    prior_lo: int                  # cached tokens before the chunk:
+    prior_hi: int                  #   uniform[prior_lo, prior_hi]
+    description: str = ""
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def replace(self, **kw) -> "PrefillConfig":
+        return dataclasses.replace(self, **kw)
+
+
+PREFILL_CONFIGS: List[PrefillConfig] = [
+    PrefillConfig(
+        "prefill_llama3_8b_bf16", 8, 32, 8, 128, chunk=512, prior_lo=0,
+        prior_hi=3584,
+        description="8 seqs, a 512-token chunk each after uniform[0,3584] "
+                    "cached tokens, 32 q / 8 KV heads, D=128, bf16"),
+]
+PREFILL_BY_NAME = {c.name: c for c in PREFILL_CONFIGS}
+
+
+@dataclass
+class PrefillCase:
+    config: PrefillConfig
+    seed: int
+    q: torch.Tensor               # [T, Hq, D] bf16, packed over sequences
+    q_start: torch.Tensor         # int32 [B+1]
+    k_pool: torch.Tensor          # chunk K/V already written
+    v_pool: torch.Tensor
+    block_tables: torch.Tensor
+    seq_lens: torch.Tensor        # cached tokens including the chunk
+    scale: float
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q_start[-1])
+
+
+def build_prefill_case(cfg: PrefillConfig, seed: int = 0,
+                       chunks: Optional[Sequence[int]] = None) -> PrefillCase:
+    """Seeded chunked-prefill input: lengths, a shuffled pool filled through
+    the block manager (prior tokens + the chunk, all written), packed
+    queries.  ``chunks`` overrides the per-sequence chunk lengths."""
+    kids = np.random.SeedSequence(seed).spawn(6)
+    rng_len = np.random.default_rng(kids[0])
+    rng_perm = np.random.default_rng(kids[1])
+    b, hkv, d = cfg.num_seqs, cfg.num_kv_heads, cfg.head_size
+    prior = rng_len.integers(cfg.prior_lo, cfg.prior_hi, size=b,
+                             endpoint=True)
+    ch = np.full(b, cfg.chunk) if chunks is None else np.asarray(chunks)
+    lens = prior + ch
+    used = int(sum(-(-int(n) // BLOCK_SIZE) for n in lens))
+    nb = used + -(-used // 10)
+    pool = BlockPool(nb, order=rng_perm.permutation(nb))
+    mgr = KVCacheManager(pool, BLOCK_SIZE)
+    for i in range(b):
+        assert mgr.admit(i, int(lens[i]))
+    tables, seq_lens = mgr.tables(range(b))
+    q_start = np.concatenate([[0], np.cumsum(ch)]).astype(np.int32)
+    q32 = _normal_f32(kids[2], (int(q_start[-1]), cfg.num_q_heads, d))
+    k32 = _normal_f32(kids[3], (nb, hkv, BLOCK_SIZE, d))
+    v32 = _normal_f32(kids[4], (nb, hkv, d, BLOCK_SIZE))
+    k_pool = _to_storage(k32, "bf16")
+    v_pool = _to_storage(v32, "bf16")
+    # slots past each sequence's length (and free blocks) hold NaN
+    written = np.zeros((nb, BLOCK_SIZE), dtype=bool)
+    for i in range(b):
+        n = int(lens[i])
+        nfull, rem = divmod(n, BLOCK_SIZE)
+        written[tables[i, :nfull]] = True
+        if rem:
+            written[tables[i, nfull], :rem] = True
+    blk_idx, tok_idx = torch.nonzero(torch.from_numpy(~written),
+                                     as_tuple=True)
+    nan = _nan_of("bf16")
+    k_pool[blk_idx, :, tok_idx, :] = nan
+    v_pool[blk_idx, :, :, tok_idx] = nan
+    return PrefillCase(
+        config=cfg, seed=seed, q=_to_storage(q32, "bf16"),
+        q_start=torch.from_numpy(q_start), k_pool=k_pool, v_pool=v_pool,
+        block_tables=torch.from_numpy(tables),
+        seq_lens=torch.from_numpy(seq_lens.astype(np.int32)),
+        scale=float(np.float32(1.0 / math.sqrt(d))))

@@ -15,7 +15,8 @@ def pytest_configure(config):
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
-from oracle.adapters import appended_pools, oracle_args, raw, raw_bits  # noqa: E402,F401
+from oracle.adapters import appended_pools, oracle_args, prefill_args, \
+    raw, raw_bits  # noqa: E402,F401
 
 
 @pytest.fixture(scope="session")

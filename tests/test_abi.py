@@ -52,6 +52,7 @@ def test_struct_layout_matches_the_header():
         "pa_decode_desc": _lib.DecodeDesc,
         "pa_append_desc": _lib.AppendDesc,
         "pa_copy_desc": _lib.CopyDesc,
+        "pa_prefill_desc": _lib.PrefillDesc,
     }
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "pa.h"',
              "int main(void) {"]
@@ -188,6 +189,37 @@ def test_copy_blocks_checks(lib):
     c.kv_dtype, c.num_pairs = _lib.PA_BF16, 0
     assert f(None, None, None, None, ctypes.byref(c), None) == 0
     assert f(p, p, p, p, None, None) == -1
+
+
+def test_prefill_checks(lib):
+    p, odd = ctypes.c_void_p(256), ctypes.c_void_p(258)
+    f = lib.pa_prefill
+
+    def desc(**kw):
+        base = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_size=128,
+                    block_size=16, num_blocks=10, max_blocks_per_seq=4,
+                    num_query_tokens=20, q_dtype=_lib.PA_BF16,
+                    kv_dtype=_lib.PA_BF16)
+        base.update(kw)
+        return _lib.PrefillDesc(**base)
+
+    one = ctypes.c_float(1.0)
+    for bad, st in [(dict(head_size=256), -3), (dict(num_q_heads=2 * 17), -3),
+                    (dict(num_q_heads=7), -3), (dict(block_size=8), -3),
+                    (dict(kv_dtype=_lib.PA_FP8_E4M3FN), -2),
+                    (dict(q_dtype=_lib.PA_F32), -2),
+                    (dict(num_query_tokens=-1), -3)]:
+        d = desc(**bad)
+        assert f(p, p, p, p, p, p, one, p, ctypes.byref(d), None) == st, bad
+    d = desc()
+    assert f(None, p, p, p, p, p, one, p, ctypes.byref(d), None) == -1
+    assert f(p, p, p, p, p, None, one, p, ctypes.byref(d), None) == -1
+    assert f(odd, p, p, p, p, p, one, p, ctypes.byref(d), None) == -4
+    assert f(p, p, p, p, p, ctypes.c_void_p(258), one, p, ctypes.byref(d),
+             None) == -4
+    e = desc(num_query_tokens=0)
+    assert f(None, None, None, None, None, None, one, None, ctypes.byref(e),
+             None) == 0
 
 
 def test_empty_calls_are_no_ops(lib):
