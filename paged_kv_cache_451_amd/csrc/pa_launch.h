@@ -75,8 +75,8 @@ hipError_t launch_kv_append_quant(const void* k_new, const void* v_new,
                                   float v_scale, hipStream_t stream);
 
 // Chunked prefill (prefill_mfma.hip): query row tiles of
-// 4 waves * 16 * kPrefillTiles rows per workgroup.
-constexpr int kPrefillTiles = 2;
+// kPrefillWaves waves * 32 rows per workgroup.
+constexpr int kPrefillWaves = 4;
 struct PrefillSched {
   int B;           // sequences
   int Hq, Hkv, G;  // heads

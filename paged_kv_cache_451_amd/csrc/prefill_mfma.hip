@@ -5,29 +5,40 @@
 // t <= p = L - C + i (causal within the chunk).  Queries are packed over
 // the batch: rows q_start[b] .. q_start[b+1] of q.
 //
-// One workgroup of kWaves waves per (tile of COLS query rows, KV head g).
-// A sequence's query rows are ordered token-major, head-minor
-// (row = i * G + n), so a tile holds consecutive tokens and all G heads
-// that share KV head g.  Each wave owns 16 * R of the tile's rows, as R
-// column tiles of the matrix-core products
+// Work split.  A sequence's query rows are ordered token-major, head-minor
+// (row = i * G + n), so a tile of COLS consecutive rows holds consecutive
+// tokens and all G heads that share KV head g.  One workgroup of kPfWaves
+// waves takes one (tile, KV head); each wave owns 32 rows.  Tiles differ in
+// cost (the keys they attend grow along the chunk and with the context), so
+// workgroups take them longest first: workgroup rank r picks the r-th tile
+// in order of decreasing step count (ties in (sequence, tile) order), found
+// by a search over step counts that every wave runs on the lengths alone.
 //
-//   S^T[32 keys][16 rows] = K[32 keys][D] . Q^T[D][16 rows]
-//   O^T[D][16 rows]      += V^T[D][32 keys] . P^T[32 keys][16 rows]
+// Products, per 64-key step, on v_mfma_f32_32x32x16_bf16:
 //
-// (v_mfma_f32_16x16x32_bf16), with the same operand layouts as the decode
-// kernel: lane (n, j) = (l % 16, l / 16) ends up owning the scores of keys
-// 8j .. 8j+7 of the step for row n, which is exactly its k-slot set of
-// P^T in the PV product, so P never moves between lanes.
+//   S^T[32 keys][32 rows] = K[32 keys][D] . Q^T[D][32 rows]      (x2)
+//   O^T[32 d][32 rows]   += V^T[32 d][16 keys] . P^T[16 keys][32 rows]
 //
-// K/V go through LDS: every step (32 keys = two 16-token blocks) the whole
-// workgroup copies the two K tiles ([16][D] each) and the two V tiles
-// ([D][16] each) of KV head g into one of two LDS buffers, while computing
-// on the other; K rows are padded by 16 bytes and V is stored as [D][32
-// keys] with rows padded to 80 bytes, so the 16-byte operand reads of a
-// wave hit distinct banks.  Keys at or past the sequence end, or in blocks
-// with an out-of-range id, get zero V (so a masked probability times them
-// is 0) and a -inf score.  The causal mask is applied only on steps that
-// reach past the smallest query position of the tile.
+// Q^T stays in registers for the whole tile.  The K rows of each 32-key
+// half are stored in LDS with bits 2 and 3 of the key index swapped, so
+// that the S^T accumulator elements 8c .. 8c+7 of lane (n, h) are the
+// scores of keys 16c + 8h .. 16c + 8h + 7 of that half: exactly lane
+// (n, h)'s slots of the P^T operand of the PV product.  P never moves
+// between lanes.
+//
+// K/V go through LDS: each step the workgroup copies the four 16-token K
+// tiles ([16][D] each) and V tiles ([D][16] each) of KV head g into one of
+// two LDS buffers while the waves compute on the other.  Rows are padded by
+// 16 bytes so the 16-byte operand reads of a wave spread over the banks.
+// Keys at or past the sequence end, or in blocks with an out-of-range id,
+// get zero V (a masked probability times them is 0) and a -inf score.  The
+// causal mask is applied only on steps that reach past the smallest query
+// position of the wave.
+//
+// Online softmax in base 2 with a lazily updated running max: the
+// accumulator is rescaled only when some row's max has grown by more than
+// 8 (log2 units) since the last rescale, so probabilities stay below 256.
+// The result is the same in exact arithmetic; only rounding differs.
 #include <math.h>
 
 #include "pa_launch.h"
@@ -37,37 +48,148 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = kPrefillWaves;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kKeys = 32;  // keys per step: two blocks
+constexpr int kRows = 32;                // query rows per wave
+constexpr int kCols = kPfWaves * kRows;  // query rows per workgroup
+constexpr int kKeys = 64;                // keys per step: four blocks
+constexpr float kLazy = 8.0f;            // rescale threshold (log2 units)
 
 template <int D>
 struct PfLds {
   static constexpr int KRow = D * 2 + 16;      // bytes per K row
-  static constexpr int VRow = kKeys * 2 + 16;  // bytes per V row [d][32]
+  static constexpr int VRow = kKeys * 2 + 16;  // bytes per V row [d][64]
   static constexpr int KBytes = kKeys * KRow;
   static constexpr int Stage = KBytes + D * VRow;
 };
 
-__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Keeps the 16-bit elements e of w (8 of them) with lo <= e < hi.
-__device__ __forceinline__ u32x4 keep_range(u32x4 w, int lo, int hi) {
+// Keeps the 16-bit elements e of w (8 of them) with e < hi.
+__device__ __forceinline__ u32x4 keep_below(u32x4 w, int hi) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const unsigned m = (2 * k >= lo && 2 * k < hi ? 0x0000FFFFu : 0u) |
-                       (2 * k + 1 >= lo && 2 * k + 1 < hi ? 0xFFFF0000u : 0u);
+    const unsigned m = (2 * k < hi ? 0x0000FFFFu : 0u) |
+                       (2 * k + 1 < hi ? 0xFFFF0000u : 0u);
     w[k] &= m;
   }
   return w;
 }
 
-template <int D, int R>
+// LDS row of key k of a step: bits 2 and 3 swapped within each 32-key half.
+__device__ __forceinline__ int k_lds_row(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+// Clamped chunk of sequence b: rows [qs, qs + C) of q, L cached tokens.
+struct Chunk {
+  int qs, C, L;
+};
+
+__device__ __forceinline__ Chunk chunk_of(const int32_t* __restrict__ q_start,
+                                          const int32_t* __restrict__ seq_lens,
+                                          int b, const PrefillSched& sc) {
+  int lo = q_start[b], hi = q_start[b + 1];
+  lo = lo < 0 ? 0 : (lo > sc.T ? sc.T : lo);
+  hi = hi < lo ? lo : (hi > sc.T ? sc.T : hi);
+  const int cap = sc.max_blocks * kBlock;
+  int L = seq_lens[b];
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  return Chunk{lo, hi - lo, L};
+}
+
+// Tiles of a chunk, and how many of them take at least W steps.  Tile t's
+// last row is min(C*G, (t+1)*COLS) - 1, its largest query position
+// L - C + that / G, and it takes ceil((position + 1) / 64) steps (0 when the
+// position is negative).  The step count does not decrease along t, so the
+// tiles taking >= W steps are a suffix.
+__device__ __forceinline__ int tiles_of(const Chunk& c, int G) {
+  return (c.C * G + kCols - 1) / kCols;
+}
+
+__device__ __forceinline__ int tiles_at_least(const Chunk& c, int G, int W) {
+  const int nt = tiles_of(c, G);
+  if (W <= 0) return nt;
+  // need position >= (W - 1) * 64, i.e. last row / G >= Y
+  const int Y = (W - 1) * kKeys - (c.L - c.C);
+  if (Y < 0) return nt;
+  if (Y >= c.C) return 0;
+  // smallest t with min(C*G, (t+1)*COLS) >= Y*G + 1
+  const int t_min = (Y * G + 1 + kCols - 1) / kCols - 1;
+  return nt - (t_min < 0 ? 0 : t_min);
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Total over all sequences of tiles_at_least(W).
+__device__ __forceinline__ int count_at_least(
+    const int32_t* __restrict__ q_start, const int32_t* __restrict__ seq_lens,
+    const PrefillSched& sc, int W) {
+  const int lane = lane_id();
+  int n = 0;
+  for (int c0 = 0; c0 < sc.B; c0 += kWave) {
+    const int b = c0 + lane;
+    if (b < sc.B)
+      n += tiles_at_least(chunk_of(q_start, seq_lens, b, sc), sc.G, W);
+  }
+  return wave_sum(n);
+}
+
+// The r-th tile in order of decreasing step count: sequence b and tile t, or
+// b = -1 when r is past the last tile.  All arguments and results uniform.
+__device__ void tile_of_rank(const int32_t* __restrict__ q_start,
+                             const int32_t* __restrict__ seq_lens,
+                             const PrefillSched& sc, int r, int* b_out,
+                             int* t_out) {
+  *b_out = -1;
+  *t_out = 0;
+  if (r >= count_at_least(q_start, seq_lens, sc, 0)) return;
+  // largest W with count_at_least(W) > r
+  int lo = 0, hi = (sc.max_blocks * kBlock + kKeys - 1) / kKeys + 1;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (count_at_least(q_start, seq_lens, sc, mid) > r)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int W = lo;
+  const int k = r - count_at_least(q_start, seq_lens, sc, W + 1);
+  // the k-th tile, in (sequence, tile) order, of those taking exactly W
+  const int lane = lane_id();
+  int carry = 0;
+  for (int c0 = 0; c0 < sc.B; c0 += kWave) {
+    const int b = c0 + lane;
+    int eq = 0, first = 0;
+    if (b < sc.B) {
+      const Chunk c = chunk_of(q_start, seq_lens, b, sc);
+      const int ge = tiles_at_least(c, sc.G, W);
+      eq = ge - tiles_at_least(c, sc.G, W + 1);
+      first = tiles_of(c, sc.G) - ge;
+    }
+    const int incl = wave_incl_scan(eq) + carry;
+    const uint64_t hit = __ballot(eq > 0 && k < incl && k >= incl - eq);
+    if (hit) {
+      const int i = __builtin_ctzll(hit);
+      *b_out = c0 + i;
+      *t_out = readlane(first, i) + k - (readlane(incl, i) - readlane(eq, i));
+      return;
+    }
+    carry = readlane(incl, kWave - 1);
+  }
+}
+
+template <int D>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k_pool,
     const __bf16* __restrict__ v_pool,
@@ -76,164 +198,150 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     const int32_t* __restrict__ q_start, __bf16* __restrict__ out,
     PrefillSched sc) {
   typedef PfLds<D> Lay;
-  constexpr int NC = D / 32;
-  constexpr int NX = D / 16;
-  constexpr int COLS = kPfWaves * 16 * R;
-  constexpr int CPT = (8 * D) / kPfThreads;  // 16-byte chunks per thread
+  constexpr int NK = D / 16;                  // 16-wide d chunks of Q^T
+  constexpr int NX = D / 32;                  // 32-row d tiles of O^T
+  constexpr int CPT = (16 * D) / kPfThreads;  // 16-byte chunks per thread
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Lay::Stage];
 
   const int tid = threadIdx.x;
+  __builtin_assume(tid < kPfThreads);
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int r16 = lane & 15;
-  const int j = lane >> 4;
+  const int n32 = lane & 31;
+  const int h = lane >> 5;
   const int g = blockIdx.x % sc.Hkv;
-  const int tile = blockIdx.x / sc.Hkv;
   const int G = sc.G;
 
-  // which sequence and which of its tiles (every wave finds the same)
-  int b = -1, t_in_b = 0;
-  {
-    int carry = 0;
-    for (int c0 = 0; c0 < sc.B && b < 0; c0 += kWave) {
-      const int bb = c0 + lane;
-      int tiles = 0;
-      if (bb < sc.B) {
-        int lo = q_start[bb], hi = q_start[bb + 1];
-        lo = lo < 0 ? 0 : (lo > sc.T ? sc.T : lo);
-        hi = hi < lo ? lo : (hi > sc.T ? sc.T : hi);
-        tiles = ((hi - lo) * G + COLS - 1) / COLS;
-      }
-      const int incl = wave_incl_scan(tiles) + carry;
-      const uint64_t hit = __ballot(bb < sc.B && tile < incl &&
-                                    tile >= incl - tiles);
-      if (hit) {
-        const int i = __builtin_ctzll(hit);
-        b = c0 + i;
-        t_in_b = tile - (readlane(incl, i) - readlane(tiles, i));
-      }
-      carry = readlane(incl, kWave - 1);
-    }
-  }
+  int b, t_in_b;
+  tile_of_rank(q_start, seq_lens, sc, blockIdx.x / sc.Hkv, &b, &t_in_b);
   if (b < 0) return;
 
-  int qs = q_start[b], qe = q_start[b + 1];
-  qs = qs < 0 ? 0 : (qs > sc.T ? sc.T : qs);
-  qe = qe < qs ? qs : (qe > sc.T ? sc.T : qe);
-  const int C = qe - qs;
-  const int cap = sc.max_blocks * kBlock;
-  int L = seq_lens[b];
-  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const Chunk ck = chunk_of(q_start, seq_lens, b, sc);
+  const int qs = ck.qs, C = ck.C, L = ck.L;
   const int rows_b = C * G;
-  const int row0 = t_in_b * COLS;
+  const int row0 = t_in_b * kCols;
   const int nblk = (L + kBlock - 1) / kBlock;
 
-  // rows of this wave: row0 + wave*16R + 16x + r16
-  int pos[R];      // query position, -1 for a row past the chunk
-  bf16x8 qb[R][NC];
+  // this lane's row: row0 + 32 * wave + n32
+  const int row = row0 + kRows * wave + n32;
+  const bool row_ok = row < rows_b;
+  const int ti = row_ok ? row / G : 0;
+  const int hn = row_ok ? row - ti * G : 0;
+  const int pos = row_ok ? L - C + ti : -1;
+  bf16x8 qb[NK];
+  {
+    const __bf16* qrow =
+        q + ((size_t)(qs + ti) * sc.Hq + (size_t)g * G + hn) * D + 8 * h;
 #pragma unroll
-  for (int x = 0; x < R; ++x) {
-    const int row = row0 + wave * 16 * R + 16 * x + r16;
-    const bool valid = row < rows_b;
-    const int i = valid ? row / G : 0;
-    const int n = valid ? row - i * G : 0;
-    pos[x] = valid ? L - C + i : -1;
-    const __bf16* qrow = q + ((size_t)(qs + i) * sc.Hq + (size_t)g * G + n) * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < NK; ++c) {
       bf16x8 z = {};
-      qb[x][c] = valid ? *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * j)
-                       : z;
+      qb[c] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 16 * c) : z;
     }
   }
-  const int last_row = (rows_b < row0 + COLS ? rows_b : row0 + COLS) - 1;
-  const int p_max = L - C + last_row / G;       // largest query position
-  const int p_min = L - C + row0 / G;           // smallest
-  const int kend = p_max + 1 < L ? p_max + 1 : L;  // keys needed
+  const int last_row = (rows_b < row0 + kCols ? rows_b : row0 + kCols) - 1;
+  const int p_max = L - C + last_row / G;  // largest query position
+  const int wp_min = L - C + (row0 + kRows * wave) / G;  // smallest, wave
+  const int kend = p_max + 1 < L ? p_max + 1 : L;        // keys needed
   const int nsteps = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
 
-  f32x4 acc[R][NX];
-  float m[R], lsum[R];
+  f32x16 acc[NX];
 #pragma unroll
-  for (int x = 0; x < R; ++x) {
-    m[x] = -INFINITY;
-    lsum[x] = 0.f;
+  for (int X = 0; X < NX; ++X)
 #pragma unroll
-    for (int X = 0; X < NX; ++X) acc[x][X] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int i = 0; i < 16; ++i) acc[X][i] = 0.f;
+  float m_run = -INFINITY, lsum = 0.f;
 
   const int32_t* trow = block_tables + (size_t)b * sc.max_blocks;
   const size_t tile_elems = (size_t)kBlock * D;
-  // valid keys of block blk (uniform): 0 past the end or for a bad id
-  auto block_valid = [&](int blk, int id) -> int {
-    if (blk >= nblk || (unsigned)id >= (unsigned)sc.NB) return 0;
-    const int v = L - blk * kBlock;
-    return v > kBlock ? kBlock : v;
+
+  // Block ids: lane u % 4 holds the entry of block 4 s + u % 4 of a step.
+  // They are loaded two steps ahead, so the K/V loads never wait on them.
+  auto table_entry = [&](int s) -> int {
+    const int blk = 4 * s + (lane & 3);
+    return trow[blk < nblk ? blk : (nblk > 0 ? nblk - 1 : 0)];
   };
 
+  // Chunk u of a thread: K chunks (u < CPT/2) then V chunks, each block's
+  // 16 x D tile being 2D chunks of 16 bytes.
+  constexpr int CH = CPT / 2;
   u32x4 regs[CPT];
-  int nv[2];
-  auto load_stage = [&](int s) {
-    int id[2];
+  int nv[4];
+  bool all_full = true;
+  auto load_stage = [&](int s, int ids_raw) {
+    int id[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int blk = 2 * s + h;
-      const int raw = trow[blk < nblk ? blk : nblk - 1];
-      nv[h] = block_valid(blk, raw);
-      id[h] = (unsigned)raw < (unsigned)sc.NB ? raw : 0;
+    for (int u = 0; u < 4; ++u) {
+      const int blk = 4 * s + u;
+      const int raw = readlane(ids_raw, u);
+      const bool ok = blk < nblk && (unsigned)raw < (unsigned)sc.NB;
+      const int v = L - blk * kBlock;
+      nv[u] = ok ? (v > kBlock ? kBlock : v) : 0;
+      id[u] = ok ? raw : 0;
     }
+    all_full = nv[0] == kBlock && nv[1] == kBlock && nv[2] == kBlock &&
+               nv[3] == kBlock;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int ch = tid + kPfThreads * u;   // [0, 8D)
-      const bool is_v = ch >= 4 * D;
-      const int w = is_v ? ch - 4 * D : ch;
-      const int h = w / (2 * D);
-      const int within = w - h * 2 * D;
-      const __bf16* pool = is_v ? v_pool : k_pool;
-      const __bf16* src = pool +
-                          ((size_t)id[h] * sc.Hkv + g) * tile_elems +
+      const int w = tid + kPfThreads * (u % CH);  // [0, 8D)
+      const int blk = w / (2 * D);
+      const int within = w - blk * 2 * D;
+      const __bf16* pool = u < CH ? k_pool : v_pool;
+      const __bf16* src = pool + ((size_t)id[blk] * sc.Hkv + g) * tile_elems +
                           (size_t)within * 8;
-      regs[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+      regs[u] = *reinterpret_cast<const u32x4*>(src);
     }
   };
   auto store_stage = [&](int buf) {
     uint8_t* base = lds + buf * Lay::Stage;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int ch = tid + kPfThreads * u;
-      const bool is_v = ch >= 4 * D;
-      const int w = is_v ? ch - 4 * D : ch;
-      const int h = w / (2 * D);
-      const int within = w - h * 2 * D;
-      if (!is_v) {
-        const int key = h * kBlock + within / (D / 8);
-        const int col = within % (D / 8);
-        *reinterpret_cast<u32x4*>(base + key * Lay::KRow + col * 16) =
-            regs[u];
-      } else {
-        const int d = within >> 1;
-        const int half = within & 1;
-        const u32x4 val = keep_range(regs[u], 0, nv[h] - 8 * half);
-        *reinterpret_cast<u32x4*>(base + Lay::KBytes + d * Lay::VRow +
-                                  (h * kBlock + half * 8) * 2) = val;
+    for (int u = 0; u < CH; ++u) {
+      const int w = tid + kPfThreads * u;
+      const int blk = w / (2 * D);
+      const int within = w - blk * 2 * D;
+      const int key = blk * kBlock + within / (D / 8);
+      const int col = within % (D / 8);
+      *reinterpret_cast<u32x4*>(base + k_lds_row(key) * Lay::KRow +
+                                col * 16) = regs[u];
+    }
+    if (all_full) {
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int w = tid + kPfThreads * u;
+        const int blk = w / (2 * D);
+        const int within = w - blk * 2 * D;
+        *reinterpret_cast<u32x4*>(base + Lay::KBytes + (within >> 1) * Lay::VRow +
+                                  (blk * kBlock + (within & 1) * 8) * 2) =
+            regs[CH + u];
+      }
+    } else {
+      // zero V past the valid tokens of each block
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int w = tid + kPfThreads * u;
+        const int blk = w / (2 * D);
+        const int within = w - blk * 2 * D;
+        const int nvb = nv[0] * (blk == 0) + nv[1] * (blk == 1) +
+                        nv[2] * (blk == 2) + nv[3] * (blk == 3);
+        const u32x4 val = keep_below(regs[CH + u], nvb - 8 * (within & 1));
+        *reinterpret_cast<u32x4*>(base + Lay::KBytes + (within >> 1) * Lay::VRow +
+                                  (blk * kBlock + (within & 1) * 8) * 2) = val;
       }
     }
   };
 
+  int ids_next = 0;  // entries of the step after the next
   if (nsteps > 0) {
-    load_stage(0);
+    load_stage(0, table_entry(0));
+    ids_next = table_entry(1);
     store_stage(0);
   }
   __syncthreads();
 
-  // lane-constant LDS offsets of the operands
-  int k_off[2];
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
-    const int key = 16 * (r16 >> 3) + 8 * ((r16 >> 2) & 1) + 4 * s2 + (r16 & 3);
-    k_off[s2] = key * Lay::KRow + 16 * j;   // + 64 c
-  }
-  const int v_off = Lay::KBytes + r16 * Lay::VRow + 16 * j;  // + 16X rows
+  // lane-constant LDS offsets of the operands: K row n32 of each 32-key
+  // half, d = 8h + 16c; V row d = n32 of each 32-row tile, keys 8h + 16c
+  const int k_off = n32 * Lay::KRow + 16 * h;
+  const int v_off = Lay::KBytes + n32 * Lay::VRow + 16 * h;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // The next stage's loads are issued unconditionally (the last step
   // reloads its own stage into the idle buffer): loads under a branch would
@@ -241,100 +349,117 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
     const bool more = s + 1 < nsteps;
-    const int nv_cur0 = nv[0], nv_cur1 = nv[1];
-    load_stage(more ? s + 1 : s);
+    int nvc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) nvc[u] = nv[u];
+    const int ids_now = ids_next;
+    load_stage(more ? s + 1 : s, ids_now);
+    ids_next = table_entry(s + 2 < nsteps ? s + 2 : s);
     const uint8_t* base = lds + buf * Lay::Stage;
 
-    bf16x8 ka[2][NC];
+    f32x16 sv[2];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+    for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        ka[s2][c] = *reinterpret_cast<const bf16x8*>(base + k_off[s2] +
-                                                     64 * c);
+      for (int i = 0; i < 16; ++i) sv[hf][i] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NK; ++c) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+            base + k_off + hf * 32 * Lay::KRow + 32 * c);
+        sv[hf] = mfma32(ka, qb[c], sv[hf]);
+      }
+    }
     const int key0 = s * kKeys;
-    const bool full = nv_cur0 == kBlock && nv_cur1 == kBlock &&
-                      key0 + kKeys - 1 <= p_min;
-    // this lane's 8 keys: key0 + 8j + e, valid in its block up to nvh
-    const int nvh = (j < 2 ? nv_cur0 : nv_cur1) - 8 * (j & 1);
-    bf16x8 pb[R];
+    const bool full = nvc[0] == kBlock && nvc[1] == kBlock &&
+                      nvc[2] == kBlock && nvc[3] == kBlock &&
+                      key0 + kKeys - 1 <= wp_min;
+    if (!full) {
+      // element 8c + j of half hf: key key0 + 32 hf + 16 c + 8 h + j, in
+      // block 2 hf + c at offset 8 h + j
 #pragma unroll
-    for (int x = 0; x < R; ++x) {
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        s0 = mfma16x16x32(ka[0][c], qb[x][c], s0);
-        s1 = mfma16x16x32(ka[1][c], qb[x][c], s1);
-      }
-      float xs[8];
+        for (int c = 0; c < 2; ++c) {
+          const int lim = pos - (key0 + 32 * hf + 16 * c + 8 * h);
+          const int nvb = nvc[2 * hf + c] - 8 * h;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xs[i] = s0[i] * sc.c_log2;
-        xs[4 + i] = s1[i] * sc.c_log2;
-      }
-      if (!full) {
-        const int lim = pos[x] - (key0 + 8 * j);  // e <= lim attends
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          xs[e] = (e <= lim && e < nvh) ? xs[e] : -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])),
-                       fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7])));
-      mx = max_xor16(mx);
-      mx = max_xor32(mx);
-      const float m_new = fmaxf(m[x], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m[x] - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 pe = (__bf16)fast_exp2(xs[e] - m_use);
-        pb[x][e] = pe;
-        psum += (float)pe;
-      }
-      lsum[x] = lsum[x] * alpha + psum;
-      m[x] = m_new;
-#pragma unroll
-      for (int X = 0; X < NX; ++X) acc[x][X] *= alpha;
+          for (int j = 0; j < 8; ++j)
+            sv[hf][8 * c + j] =
+                (j <= lim && j < nvb) ? sv[hf][8 * c + j] : -INFINITY;
+        }
     }
+    float mx = -INFINITY;
 #pragma unroll
-    for (int X = 0; X < NX; ++X) {
-      const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-          base + v_off + 16 * X * Lay::VRow);
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int x = 0; x < R; ++x) acc[x][X] = mfma16x16x32(va, pb[x], acc[x][X]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[hf][i]);
+    mx = max_xor32(mx);
+    const float m_cand = mx * sc.c_log2;
+    // rescale when some row's max grew by more than kLazy (or was unset)
+    if (__ballot(m_cand > m_run + kLazy ||
+                 (m_run == -INFINITY && m_cand > -INFINITY))) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha =
+          fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      lsum *= alpha;
+#pragma unroll
+      for (int X = 0; X < NX; ++X) acc[X] *= alpha;
+      m_run = m_new;
     }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const __bf16 p0 = (__bf16)fast_exp2(
+              fmaf(sv[hf][8 * c + j], sc.c_log2, -m_use));
+          const __bf16 p1 = (__bf16)fast_exp2(
+              fmaf(sv[hf][8 * c + j + 1], sc.c_log2, -m_use));
+          pb[hf][c][j] = p0;
+          pb[hf][c][j + 1] = p1;
+          const bf16x2 pp = {p0, p1};
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+        }
+#pragma unroll
+    for (int X = 0; X < NX; ++X)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(
+              base + v_off + X * 32 * Lay::VRow + (32 * hf + 16 * c) * 2);
+          acc[X] = mfma32(va, pb[hf][c], acc[X]);
+        }
     store_stage(buf ^ 1);
     __syncthreads();
   }
 
-  // lane (n, j) holds O[row n][16X + 4j + i]
-#pragma unroll
-  for (int x = 0; x < R; ++x) {
-    float ltot = lsum[x] + __shfl_xor(lsum[x], 16, kWave);
-    ltot += __shfl_xor(ltot, 32, kWave);
-    const int row = row0 + wave * 16 * R + 16 * x + r16;
-    if (row >= rows_b) continue;
-    const int i = row / G;
-    const int n = row - i * G;
+  // lane (n, h) holds O[row n][32 X + 8 a + 4 h + i] in element 4 a + i
+  const float ltot = lsum + __shfl_xor(lsum, 32, kWave);
+  if (row_ok) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    __bf16* orow = out + ((size_t)(qs + i) * sc.Hq + (size_t)g * G + n) * D +
-                   4 * j;
+    __bf16* orow =
+        out + ((size_t)(qs + ti) * sc.Hq + (size_t)g * G + hn) * D + 4 * h;
 #pragma unroll
-    for (int X = 0; X < NX; ++X) {
-      bf16x4 o;
+    for (int X = 0; X < NX; ++X)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = (__bf16)(acc[x][X][k] * inv);
-      *reinterpret_cast<bf16x4*>(orow + 16 * X) = o;
-    }
+      for (int a = 0; a < 4; ++a) {
+        bf16x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc[X][4 * a + i] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * X + 8 * a) = o;
+      }
   }
 }
 
-template <int D, int R>
+template <int D>
 void launch_pf(const PrefillArgs& a, hipStream_t stream) {
-  constexpr int COLS = kPfWaves * 16 * R;
-  const int tiles = (int)(((int64_t)a.s.T * a.s.G + COLS - 1) / COLS) + a.s.B;
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, R>),
+  const int tiles =
+      (int)(((int64_t)a.s.T * a.s.G + kCols - 1) / kCols) + a.s.B;
+  hipLaunchKernelGGL((prefill_mfma_kernel<D>),
                      dim3((unsigned)(tiles * a.s.Hkv)), dim3(kPfThreads), 0,
                      stream, reinterpret_cast<const __bf16*>(a.q),
                      reinterpret_cast<const __bf16*>(a.k_pool),
@@ -346,17 +471,16 @@ void launch_pf(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 int64_t prefill_grid(int head_size, int64_t T, int G, int B, int Hkv) {
-  const int cols = kPfWaves * 16 * kPrefillTiles;
   (void)head_size;
-  return ((T * G + cols - 1) / cols + B) * Hkv;
+  return ((T * G + kCols - 1) / kCols + B) * Hkv;
 }
 
 hipError_t launch_prefill(int head_size, const PrefillArgs& a,
                           hipStream_t stream) {
   if (a.s.B == 0 || a.s.T == 0) return hipSuccess;
   switch (head_size) {
-    case 64: launch_pf<64, kPrefillTiles>(a, stream); break;
-    case 128: launch_pf<128, kPrefillTiles>(a, stream); break;
+    case 64: launch_pf<64>(a, stream); break;
+    case 128: launch_pf<128>(a, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
