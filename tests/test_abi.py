@@ -217,6 +217,9 @@ def test_prefill_checks(lib):
     assert f(odd, p, p, p, p, p, one, p, ctypes.byref(d), None) == -4
     assert f(p, p, p, p, p, ctypes.c_void_p(258), one, p, ctypes.byref(d),
              None) == -4
+    for bad_scale in (0.0, -0.5, float("nan"), float("inf")):
+        assert f(p, p, p, p, p, p, ctypes.c_float(bad_scale), p,
+                 ctypes.byref(d), None) == -3, bad_scale
     e = desc(num_query_tokens=0)
     assert f(None, None, None, None, None, None, one, None, ctypes.byref(e),
              None) == 0
