@@ -50,6 +50,11 @@ def parse():
     p.add_argument("--unfused", action="store_true",
                    help="time the step as three launches (pa_kv_append, "
                         "then pa_decode) instead of pa_decode_append")
+    p.add_argument("--shared-prefix", default="auto",
+                   choices=["auto", "on", "off"],
+                   help="cascade decode (pa_decode_append_shared: a shared "
+                        "prompt prefix read once for the whole batch): auto "
+                        "= on for the prefix-shared workload")
     p.add_argument("--op", default="step",
                    choices=["step", "append", "append_quant",
                             "copy_blocks", "engine", "prefill"],
@@ -64,6 +69,12 @@ def parse():
                    help="block pairs copied per launch by --op copy_blocks")
     p.add_argument("--tokens", type=int, default=32768,
                    help="tokens written per launch by --op append*")
+    p.add_argument("--slots", default="scattered",
+                   choices=["scattered", "runs"],
+                   help="slot pattern of --op append*: scattered (a random "
+                        "set of distinct slots, one token per block as in a "
+                        "decode step) or runs (whole blocks filled in order, "
+                        "as a prefill chunk writes them)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the bench, run three plain 1 GiB device "
                         "copies (the reference kernel that scales HBM "
@@ -163,8 +174,10 @@ def _kernel_events(torch, n):
 def bench_append(a, torch, _lib):
     """Throughput of writing many new tokens into a pool (a prefill chunk's
     KV): --op append copies bf16 rows into a bf16 pool, --op append_quant
-    quantises bf16 rows into an fp8 e4m3fn pool.  Slots are a seeded random
-    set of distinct slots of the pool, so rows land in scattered blocks."""
+    quantises bf16 rows into an fp8 e4m3fn pool.  --slots scattered takes a
+    seeded random set of distinct slots (rows land in scattered blocks, each
+    V element a separate 2- or 1-byte store); --slots runs fills whole blocks
+    of a shuffled pool in order, as a prefill chunk does."""
     import numpy as np
 
     quant = a.op == "append_quant"
@@ -175,8 +188,14 @@ def bench_append(a, torch, _lib):
     g = torch.Generator().manual_seed(a.seed or 0)
     k_new = torch.randn(a.tokens, hkv, d, generator=g).to(torch.bfloat16)
     v_new = torch.randn(a.tokens, hkv, d, generator=g).to(torch.bfloat16)
-    slots = torch.from_numpy(np.random.default_rng(a.seed or 0).permutation(
-        nb * 16)[:a.tokens].astype(np.int32))
+    rng = np.random.default_rng(a.seed or 0)
+    if a.slots == "runs":
+        t = np.arange(a.tokens)
+        slots = torch.from_numpy(
+            (rng.permutation(nb)[t // 16] * 16 + t % 16).astype(np.int32))
+    else:
+        slots = torch.from_numpy(
+            rng.permutation(nb * 16)[:a.tokens].astype(np.int32))
     pool_dtype = torch.float8_e4m3fn if quant else torch.bfloat16
     kp = torch.zeros(nb, hkv, 16, d, dtype=torch.uint8 if quant
                      else torch.bfloat16, device=dev).view(pool_dtype)
@@ -239,7 +258,8 @@ def bench_append(a, torch, _lib):
         "ms_per_step": round(avg, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16->fp8" if quant else "bf16", "data": "synthetic",
-        "config": {"workload": f"append {a.tokens} tokens", "tokens": a.tokens,
+        "config": {"workload": f"append {a.tokens} tokens, {a.slots} slots",
+                   "tokens": a.tokens, "slots": a.slots,
                    "num_kv_heads": hkv, "head_size": d, "pool_blocks": nb},
         "roofline": {"bound": "hbm", "kernel": "kv_append_quant_kernel"
                      if quant else "kv_append_kernel",
@@ -566,13 +586,34 @@ def main():
             events=events)
 
     fused = not a.unfused
+    cascade = fused and cfg.prefix_len > 0 and a.shared_prefix != "off"
+    if a.shared_prefix == "on" and not cascade:
+        print("--shared-prefix on needs the fused step and a workload with a "
+              "shared prefix", file=sys.stderr)
+        sys.exit(2)
+    shared = None
+    if cascade:
+        # every sequence shares the prompt's full blocks at the head of its
+        # table (the block manager found them by hash)
+        pb = cfg.prefix_len // 16
+        shared = (torch.tensor([0, cfg.num_seqs], dtype=torch.int32,
+                               device=dev),
+                  torch.tensor([pb], dtype=torch.int32, device=dev))
+        hint = case.total_blocks - cfg.num_seqs * pb
+
+        def desc_for(events=None):  # noqa: F811 (suffix blocks as the hint)
+            return _lib.decode_desc(
+                q, kps[0], tables, max_seq_len=case.max_seq_len,
+                total_blocks_hint=hint, num_waves=a.num_waves,
+                events=events)
     base_desc = desc_for()
-    ws = _lib.alloc_workspace(base_desc, dev, fused=fused)
+    ws = _lib.alloc_workspace(base_desc, dev, fused=fused, shared=cascade)
 
     def prepared(i, desc):
         kp, vp = kps[i % nrot], vps[i % nrot]
         return _lib.PreparedStep(q, kp, vp, tables, lens, case.scale, out,
-                                 desc, ws, k_new, v_new, slots, fused=fused)
+                                 desc, ws, k_new, v_new, slots, fused=fused,
+                                 shared=shared)
 
     warm = [prepared(i, base_desc) for i in range(a.warmup)]
     timed = [prepared(a.warmup + i, base_desc) for i in range(a.steps)]
@@ -593,13 +634,22 @@ def main():
     # the dominant kernel alone: HIP events recorded on the launch stream
     # right before and after each main decode kernel (events serialise the
     # stream, so this runs as its own region after the timed one)
-    roof = [_lib.PreparedStep(q, kps[i % nrot], vps[i % nrot], tables, lens,
-                              case.scale, out,
-                              desc_for((e0.cuda_event, e1.cuda_event)), ws,
-                              k_new, v_new, slots, fused=fused)
-            for i, (e0, e1) in enumerate(ev)]
-    for step in roof:
-        step()
+    if cascade:
+        # four launches share the work: time the whole step with events
+        # around each call on the launch stream
+        roof = [prepared(i, base_desc) for i in range(len(ev))]
+        for step, (e0, e1) in zip(roof, ev):
+            e0.record(stream)
+            step()
+            e1.record(stream)
+    else:
+        roof = [_lib.PreparedStep(q, kps[i % nrot], vps[i % nrot], tables,
+                                  lens, case.scale, out,
+                                  desc_for((e0.cuda_event, e1.cuda_event)),
+                                  ws, k_new, v_new, slots, fused=fused)
+                for i, (e0, e1) in enumerate(ev)]
+        for step in roof:
+            step()
     torch.cuda.synchronize()
     kern_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     kern_ms.sort()
@@ -608,8 +658,16 @@ def main():
 
     value = nbytes["step"] / (ms_step * 1e-3) / 1e9
     main_bytes = nbytes["main_fused"] if fused else nbytes["decode"]
+    kernel_name = ("decode_mfma_kernel" if cfg.kv_dtype != "f32"
+                   else "decode_valu_kernel")
+    if cascade:
+        # the whole step, against the bytes it must move: each physical
+        # block once, q, out, tables, and the append
+        main_bytes = nbytes["decode_unique"] + nbytes["append"]
+        kernel_name = ("cascade step (suffix tables, shared-prefix pass, "
+                       "main pass, merge/append)")
     achieved = main_bytes / (k_avg * 1e-3) / 1e9
-    traffic = measured_traffic(cfg.name)
+    traffic = None if cascade else measured_traffic(cfg.name)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -631,7 +689,9 @@ def main():
             "context_tokens": nbytes["context_tokens"],
             "max_seq_len": case.max_seq_len, "num_blocks": case.num_blocks,
             "seed": seed, "pool_copies_rotated": nrot,
-            "step": ("pa_decode_append (append fused into decode)" if fused
+            "step": ("pa_decode_append_shared (cascade: the shared prefix "
+                     "read once per batch)" if cascade else
+                     "pa_decode_append (append fused into decode)" if fused
                      else "pa_kv_append + pa_decode"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -641,8 +701,7 @@ def main():
         "bytes_per_step": nbytes["step"],
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_mfma_kernel" if cfg.kv_dtype != "f32"
-            else "decode_valu_kernel",
+            "kernel": kernel_name,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

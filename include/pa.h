@@ -201,6 +201,61 @@ int pa_decode_append(const void* q, void* k_pool, void* v_pool,
                      size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of workspace that pa_decode_append_shared needs (0 on an invalid
+ * descriptor): that of pa_decode_append plus a suffix block table
+ * (num_seqs x max_blocks_per_seq int32), num_seqs suffix lengths, and one
+ * fp32 partial of head_size + 2 values per (sequence, query head).
+ */
+size_t pa_decode_append_shared_workspace_size(const pa_decode_desc* desc);
+
+/*
+ * Cascade form of pa_decode_append for batches whose sequences share a
+ * prompt prefix.  Sequences that share full prefix blocks hold the same
+ * physical blocks at the head of their tables ("PagedAttention：KV cache
+ * 即虚拟内存（block manager & 碎片）", section "深入原理", sharing bullet),
+ * and paged attention over such a table equals dense attention over the
+ * contiguous context (same page, section "直接答案"), so the softmax splits
+ * exactly into the shared part and each sequence's own part.  This call
+ * reads each shared prefix once per group: a matrix-core pass attends every
+ * member's query to its group's prefix blocks (one fp32 partial per
+ * sequence and query head), the ordinary main pass attends each sequence's
+ * remaining blocks, and the merge pass folds both with the appended token.
+ *   group_start          int32 [num_groups + 1], device, non-decreasing:
+ *                        group j is sequences group_start[j] ..
+ *                        group_start[j+1] - 1; sequences outside every
+ *                        group have no shared part.
+ *   group_prefix_blocks  int32 [num_groups], device: P_j, the number of
+ *                        leading table entries that every member of group
+ *                        j shares (read through the first member's row).
+ *   num_groups           0 .. num_seqs; 0 is pa_decode_append (the group
+ *                        arrays may then be NULL).
+ *   workspace            at least
+ *                        pa_decode_append_shared_workspace_size(desc)
+ *                        bytes, 256-byte aligned.
+ * Other arguments as for pa_decode_append; only bf16 q and bf16 pools,
+ * head_size 64 or 128, and scale > 0 are supported.  total_blocks_hint, if
+ * given, should count the suffix blocks.  The caller guarantees that the
+ * members' first P_j entries are equal; if they are not, the prefix of the
+ * first member is used for all (memory-safe, numerically the first
+ * member's prefix).  The shared part ends where the first member's tokens
+ * before its newest end, if that is earlier than 16 P_j; a member shorter
+ * than the shared part attends only its own tokens before its newest.
+ * Errors: as pa_decode_append; PA_ERR_DTYPE for other dtypes; PA_ERR_SHAPE
+ * for head_size, num_groups or scale out of range; PA_ERR_NULL /
+ * PA_ERR_ALIGN for missing or misaligned group arrays.
+ */
+int pa_decode_append_shared(const void* q, void* k_pool, void* v_pool,
+                            const int32_t* block_tables,
+                            const int32_t* seq_lens, float scale, void* out,
+                            const void* k_new, const void* v_new,
+                            const int32_t* slot_mapping,
+                            const int32_t* group_start,
+                            const int32_t* group_prefix_blocks,
+                            int32_t num_groups, const pa_decode_desc* desc,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * Shapes of one append call.
  *   num_tokens    N >= 0
  *   num_kv_heads  Hkv >= 1

@@ -25,7 +25,8 @@ _DTYPE = {
 
 # names every build of the library exports (checked by the tests)
 EXPORTS = ("pa_decode", "pa_decode_workspace_size", "pa_decode_append",
-           "pa_decode_append_workspace_size", "pa_kv_append",
+           "pa_decode_append_workspace_size", "pa_decode_append_shared",
+           "pa_decode_append_shared_workspace_size", "pa_kv_append",
            "pa_kv_append_quant", "pa_copy_blocks", "pa_prefill",
            "pa_status_string", "pa_abi_version")
 
@@ -114,6 +115,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      vp, vp, vp, ctypes.POINTER(DecodeDesc),
                                      vp, sz, vp]
     lib.pa_decode_append.restype = ctypes.c_int
+    lib.pa_decode_append_shared_workspace_size.argtypes = [
+        ctypes.POINTER(DecodeDesc)]
+    lib.pa_decode_append_shared_workspace_size.restype = sz
+    lib.pa_decode_append_shared.argtypes = [
+        vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp,
+        ctypes.c_int32, ctypes.POINTER(DecodeDesc), vp, sz, vp]
+    lib.pa_decode_append_shared.restype = ctypes.c_int
     lib.pa_kv_append.argtypes = [vp, vp, vp, vp, vp,
                                  ctypes.POINTER(AppendDesc), vp]
     lib.pa_kv_append.restype = ctypes.c_int
@@ -178,16 +186,21 @@ def decode_desc(q: torch.Tensor, k_pool: torch.Tensor,
     return desc
 
 
-def workspace_size(desc: DecodeDesc, fused: bool = False) -> int:
+def workspace_size(desc: DecodeDesc, fused: bool = False,
+                   shared: bool = False) -> int:
     lib = load()
-    fn = lib.pa_decode_append_workspace_size if fused else \
-        lib.pa_decode_workspace_size
+    if shared:
+        fn = lib.pa_decode_append_shared_workspace_size
+    elif fused:
+        fn = lib.pa_decode_append_workspace_size
+    else:
+        fn = lib.pa_decode_workspace_size
     return int(fn(ctypes.byref(desc)))
 
 
-def alloc_workspace(desc: DecodeDesc, device=None,
-                    fused: bool = False) -> torch.Tensor:
-    n = max(workspace_size(desc, fused), 256)
+def alloc_workspace(desc: DecodeDesc, device=None, fused: bool = False,
+                    shared: bool = False) -> torch.Tensor:
+    n = max(workspace_size(desc, fused, shared), 256)
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 
 
@@ -234,6 +247,33 @@ def pa_decode_append(q, k_pool, v_pool, block_tables, seq_lens, scale, out,
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
         _ptr(seq_lens), ctypes.c_float(scale), _ptr(out), _ptr(k_new),
         _ptr(v_new), _ptr(slot_mapping), ctypes.byref(desc), _ptr(workspace),
+        workspace.numel(), _stream()))
+    return out
+
+
+def pa_decode_append_shared(q, k_pool, v_pool, block_tables, seq_lens, scale,
+                            out, k_new, v_new, slot_mapping, group_start,
+                            group_prefix_blocks, *, max_seq_len: int,
+                            total_blocks_hint: int = 0, num_waves: int = 0,
+                            workspace: Optional[torch.Tensor] = None,
+                            events: Optional[Sequence] = None,
+                            desc: Optional[DecodeDesc] = None
+                            ) -> torch.Tensor:
+    """Cascade form of the fused step: shared prompt prefixes read once per
+    group of sequences (see ``include/pa.h``)."""
+    lib = load()
+    if desc is None:
+        desc = decode_desc(q, k_pool, block_tables, max_seq_len=max_seq_len,
+                           total_blocks_hint=total_blocks_hint,
+                           num_waves=num_waves, events=events)
+    if workspace is None:
+        workspace = alloc_workspace(desc, q.device, fused=True, shared=True)
+    ng = 0 if group_start is None else group_start.numel() - 1
+    _check(lib.pa_decode_append_shared(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        _ptr(seq_lens), ctypes.c_float(scale), _ptr(out), _ptr(k_new),
+        _ptr(v_new), _ptr(slot_mapping), _ptr(group_start),
+        _ptr(group_prefix_blocks), ng, ctypes.byref(desc), _ptr(workspace),
         workspace.numel(), _stream()))
     return out
 
@@ -314,12 +354,24 @@ class PreparedStep:
     def __init__(self, q, k_pool, v_pool, block_tables, seq_lens, scale, out,
                  desc: DecodeDesc, workspace: torch.Tensor,
                  k_new=None, v_new=None, slot_mapping=None,
-                 fused: bool = False):
+                 fused: bool = False, shared=None):
         lib = load()
         self._keep = (q, k_pool, v_pool, block_tables, seq_lens, out,
-                      workspace, k_new, v_new, slot_mapping, desc)
+                      workspace, k_new, v_new, slot_mapping, desc, shared)
         stream = _stream()
         self._append = None
+        if shared is not None:  # (group_start, group_prefix_blocks)
+            if k_new is None:
+                raise ValueError("the cascade step needs k_new/v_new/slots")
+            gs, gp = shared
+            self._decode = lib.pa_decode_append_shared
+            self._decode_args = (
+                _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
+                _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(gs),
+                _ptr(gp), gs.numel() - 1, ctypes.byref(desc),
+                _ptr(workspace), workspace.numel(), stream)
+            return
         if fused:
             if k_new is None:
                 raise ValueError("the fused step needs k_new/v_new/slots")

@@ -164,6 +164,9 @@ struct KvElem<1> {
 //                            (sum_i w_i l_i + 2^(s-M)).
 // The pool slot is not read by this call's main pass (its position is at or
 // past the attended length), so the write needs no ordering with it.
+// In cascade decode the main pass covered only each sequence's suffix
+// blocks; the shared-prefix pass's partial is folded in as one more term
+// (when it holds any weight), and `full_lens` gives the true lengths.
 template <int KB, int D>
 __global__ __launch_bounds__(64) void decode_merge_append_kernel(
     typename KvElem<KB>::io* __restrict__ out_all,
@@ -176,7 +179,8 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(
     typename KvElem<KB>::raw* __restrict__ v_pool,
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const float* __restrict__ direct_ml, const float* __restrict__ direct_o,
-    Sched s) {
+    const float* __restrict__ shared_ml, const float* __restrict__ shared_o,
+    int shared_splits, const int32_t* __restrict__ full_lens, Sched s) {
   typedef KvElem<KB> E;
   typedef typename E::io OT;
   typedef typename E::raw RT;
@@ -194,8 +198,22 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(
   const int Sb = prefix[b];
   const int Sb1 = prefix[b + 1];
   const int U = prefix[s.B];
-  const int L = seq_lens[b];
+  const int L = full_lens ? full_lens[b] : seq_lens[b];
   const int slot = slots[b];
+  // shared-prefix partials, one per key range (all issued up front)
+  float sh_m[kMaxSharedSplits], sh_l[kMaxSharedSplits];
+  float sh_o[kMaxSharedSplits][NR];
+  const size_t split_rows = (size_t)s.B * s.Hq;
+#pragma unroll
+  for (int k = 0; k < kMaxSharedSplits; ++k) {
+    const bool live = shared_ml && k < shared_splits;
+    const size_t r = (size_t)k * split_rows + h_row;
+    sh_m[k] = live ? shared_ml[r * 2] : -INFINITY;
+    sh_l[k] = live ? shared_ml[r * 2 + 1] : 0.f;
+#pragma unroll
+    for (int x = 0; x < NR; ++x)
+      sh_o[k][x] = live ? shared_o[r * D + lane + 64 * x] : 0.f;
+  }
   RT kr[NR], vr[NR];
   float qf[NR];
 #pragma unroll
@@ -238,6 +256,29 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(
     } else {
       fold_range_partials<D>(kf, kl, Sb, U, g, n, s, part_ml, part_o, M,
                              lsum, o);
+    }
+  }
+  if (shared_ml) {  // the shared prefix's partials, as more terms
+    float m_new = M;
+#pragma unroll
+    for (int k = 0; k < kMaxSharedSplits; ++k)
+      if (sh_l[k] > 0.f) m_new = fmaxf(m_new, sh_m[k]);
+    if (m_new > -INFINITY) {
+      const float alpha = fast_exp2(M - m_new);
+      lsum *= alpha;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) o[r] *= alpha;
+#pragma unroll
+      for (int k = 0; k < kMaxSharedSplits; ++k) {
+        // a range with no weight is skipped, not multiplied by zero: its
+        // output row was never written
+        if (!(sh_l[k] > 0.f)) continue;
+        const float w = fast_exp2(sh_m[k] - m_new);
+        lsum = fmaf(w, sh_l[k], lsum);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) o[r] = fmaf(w, sh_o[k][r], o[r]);
+      }
+      M = m_new;
     }
   }
   if (L >= 1) {  // the newest token, from k_new / v_new
@@ -288,7 +329,8 @@ void launch_append_one(const DecodeArgs& a, hipStream_t stream) {
       reinterpret_cast<const typename E::raw*>(a.v_new),
       reinterpret_cast<typename E::raw*>(a.k_pool_w),
       reinterpret_cast<typename E::raw*>(a.v_pool_w), a.part_ml, a.part_o,
-      a.direct_ml, a.direct_o, a.s);
+      a.direct_ml, a.direct_o, a.shared_ml, a.shared_o, a.shared_splits,
+      a.full_lens, a.s);
 }
 
 template <int KB>

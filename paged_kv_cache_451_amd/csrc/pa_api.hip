@@ -89,12 +89,16 @@ struct Plan {
   int Wh;  // ranges per KV head
   int W;   // workgroups of the main pass
   size_t off_ml, off_o, off_dml, off_do, bytes;
+  // cascade decode: suffix tables and lengths, shared-prefix partials
+  size_t off_st, off_sl, off_sml, off_so;
+  int splits;  // key ranges per group of the shared-prefix pass
 };
 
 // Ranges per KV head: enough resident workgroups to fill every CU, but no
 // range shorter than kMinBlocksPerRange blocks when the total is known or
 // bounded.
-bool make_plan(const pa_decode_desc* d, bool fused, Plan* p) {
+bool make_plan(const pa_decode_desc* d, bool fused, Plan* p,
+               bool cascade = false) {
   const int hkv = d->num_kv_heads;
   const int G = d->num_q_heads / hkv;
   int64_t wh;
@@ -135,19 +139,68 @@ bool make_plan(const pa_decode_desc* d, bool fused, Plan* p) {
     p->off_do = p->off_dml + round_up(hrows * 2 * sizeof(float));
     p->bytes = p->off_do + round_up(hrows * d->head_size * sizeof(float));
   }
+  p->off_st = p->off_sl = p->off_sml = p->off_so = 0;
+  p->splits = 1;
+  if (cascade) {
+    // Key ranges per shared prefix: about one workgroup per CU when one
+    // group covers the batch (measured on MI355X with a 128-sequence batch
+    // sharing 2048 tokens: two per CU or a half per CU is slower, the first
+    // by the extra partials the merge reads), at least two 64-key steps per
+    // range of the longest possible prefix, at most kMaxSharedSplits.
+    const int cus = cu_count();
+    if (cus <= 0) return false;
+    const int64_t tiles =
+        ((int64_t)d->num_seqs * G + pa::kPrefillWaves * 32 - 1) /
+            (pa::kPrefillWaves * 32) + 1;
+    int64_t ns = ((int64_t)cus + tiles * hkv - 1) / (tiles * hkv);
+    const int64_t steps_cap = ((d->max_seq_len + 63) / 64 + 1) / 2;
+    if (ns > steps_cap) ns = steps_cap;
+    if (ns > pa::kMaxSharedSplits) ns = pa::kMaxSharedSplits;
+    if (ns < 1) ns = 1;
+    p->splits = (int)ns;
+    const size_t hrows = (size_t)d->num_seqs * d->num_q_heads * ns;
+    p->off_st = p->bytes;
+    p->off_sl = p->off_st + round_up((size_t)d->num_seqs *
+                                     d->max_blocks_per_seq * sizeof(int32_t));
+    p->off_sml = p->off_sl + round_up((size_t)d->num_seqs * sizeof(int32_t));
+    p->off_so = p->off_sml + round_up(hrows * 2 * sizeof(float));
+    p->bytes = p->off_so + round_up(hrows * d->head_size * sizeof(float));
+  }
   return true;
 }
 
-// Both decode entry points; k_new == nullptr selects the plain decode.
+// Groups of a cascade decode call (device arrays).
+struct SharedPrefix {
+  const int32_t* group_start;          // [num_groups + 1]
+  const int32_t* group_prefix_blocks;  // [num_groups]
+  int num_groups;
+};
+
+// All decode entry points; k_new == nullptr selects the plain decode, sp
+// the cascade form of the fused step.
 int run_decode(const void* q, const void* k_pool, const void* v_pool,
                const int32_t* block_tables, const int32_t* seq_lens,
                float scale, void* out, const void* k_new, const void* v_new,
                const int32_t* slots, void* k_pool_w, void* v_pool_w,
                const pa_decode_desc* desc, void* workspace,
-               size_t workspace_bytes, void* stream) {
+               size_t workspace_bytes, void* stream,
+               const SharedPrefix* sp = nullptr) {
   int st = check_desc(desc);
   if (st != PA_OK) return st;
   const bool fused = k_new != nullptr;
+  if (sp) {
+    if (desc->q_dtype != PA_BF16 || desc->kv_dtype != PA_BF16)
+      return PA_ERR_DTYPE;
+    if ((desc->head_size != 64 && desc->head_size != 128) ||
+        sp->num_groups < 0 || sp->num_groups > desc->num_seqs)
+      return PA_ERR_SHAPE;
+    if (!(scale > 0.f)) return PA_ERR_SHAPE;
+    const int G = desc->num_q_heads / desc->num_kv_heads;
+    if (pa::prefill_grid(desc->head_size, desc->num_seqs, G, sp->num_groups,
+                         desc->num_kv_heads) * pa::kMaxSharedSplits +
+            desc->num_seqs > INT32_MAX)
+      return PA_ERR_SHAPE;
+  }
   if (desc->num_seqs == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out)
     return PA_ERR_NULL;
@@ -159,8 +212,14 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
                 ((uintptr_t)slots & 3u)))
     return PA_ERR_ALIGN;
   if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (sp && sp->num_groups > 0) {
+    if (!sp->group_start || !sp->group_prefix_blocks) return PA_ERR_NULL;
+    if (((uintptr_t)sp->group_start & 3u) ||
+        ((uintptr_t)sp->group_prefix_blocks & 3u))
+      return PA_ERR_ALIGN;
+  }
   Plan p;
-  if (!make_plan(desc, fused, &p)) return PA_ERR_DEVICE;
+  if (!make_plan(desc, fused, &p, sp != nullptr)) return PA_ERR_DEVICE;
   if (!workspace || workspace_bytes < p.bytes) return PA_ERR_WORKSPACE;
   if ((uintptr_t)workspace % kAlign) return PA_ERR_ALIGN;
 
@@ -193,8 +252,52 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
   a.s.G = desc->num_q_heads / desc->num_kv_heads;
   a.s.Wh = p.Wh;
   a.s.len_bias = fused ? 1 : 0;
+  a.shared_ml = nullptr;
+  a.shared_o = nullptr;
+  a.shared_splits = 0;
+  a.full_lens = nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sp && sp->num_groups > 0) {
+    // one launch reads the shared prefixes once per group and writes the
+    // suffix view of every sequence; the main and merge passes below run
+    // on the suffixes
+    int32_t* st_tab = reinterpret_cast<int32_t*>(ws + p.off_st);
+    int32_t* st_len = reinterpret_cast<int32_t*>(ws + p.off_sl);
+    float* sml = reinterpret_cast<float*>(ws + p.off_sml);
+    float* so = reinterpret_cast<float*>(ws + p.off_so);
+    pa::PrefillArgs pf;
+    pf.q = q;
+    pf.k_pool = k_pool;
+    pf.v_pool = v_pool;
+    pf.block_tables = block_tables;
+    pf.seq_lens = sp->group_prefix_blocks;
+    pf.q_start = sp->group_start;
+    pf.out = nullptr;
+    pf.member_lens = seq_lens;
+    pf.part_ml = sml;
+    pf.part_o = so;
+    pf.suffix_tables = st_tab;
+    pf.suffix_lens = st_len;
+    pf.s.B = sp->num_groups;
+    pf.s.Hq = desc->num_q_heads;
+    pf.s.Hkv = desc->num_kv_heads;
+    pf.s.G = a.s.G;
+    pf.s.max_blocks = desc->max_blocks_per_seq;
+    pf.s.NB = desc->num_blocks;
+    pf.s.T = desc->num_seqs;
+    pf.s.c_log2 = a.s.c_log2;
+    pf.s.splits = p.splits;
+    const hipError_t e = pa::launch_shared_prefix(desc->head_size, pf, s);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+
+    a.block_tables = st_tab;
+    a.seq_lens = st_len;
+    a.full_lens = seq_lens;
+    a.shared_ml = sml;
+    a.shared_o = so;
+    a.shared_splits = p.splits;
+  }
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(
       const_cast<void**>(desc->profile_events));
   if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return PA_ERR_LAUNCH;
@@ -273,6 +376,34 @@ int pa_decode_append(const void* q, void* k_pool, void* v_pool,
   return run_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out,
                     k_new, v_new, slot_mapping, k_pool, v_pool, desc,
                     workspace, workspace_bytes, stream);
+}
+
+size_t pa_decode_append_shared_workspace_size(const pa_decode_desc* desc) {
+  if (check_desc(desc) != PA_OK) return 0;
+  if (desc->num_seqs == 0) return 0;
+  Plan p;
+  if (!make_plan(desc, true, &p, true)) return 0;
+  return p.bytes;
+}
+
+int pa_decode_append_shared(const void* q, void* k_pool, void* v_pool,
+                            const int32_t* block_tables,
+                            const int32_t* seq_lens, float scale, void* out,
+                            const void* k_new, const void* v_new,
+                            const int32_t* slot_mapping,
+                            const int32_t* group_start,
+                            const int32_t* group_prefix_blocks,
+                            int32_t num_groups, const pa_decode_desc* desc,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!desc) return PA_ERR_NULL;
+  if (desc->num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
+    return PA_ERR_NULL;
+  if (desc->num_seqs == 0) return check_desc(desc);
+  SharedPrefix sp{group_start, group_prefix_blocks, num_groups};
+  return run_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out,
+                    k_new, v_new, slot_mapping, k_pool, v_pool, desc,
+                    workspace, workspace_bytes, stream, &sp);
 }
 
 int pa_kv_append(const void* k_new, const void* v_new,
@@ -416,6 +547,13 @@ int pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   a.s.NB = d->num_blocks;
   a.s.T = d->num_query_tokens;
   a.s.c_log2 = (float)((double)scale * 1.4426950408889634);
+  a.s.splits = 1;
+  a.s.attn_grid = 0;
+  a.member_lens = nullptr;
+  a.suffix_tables = nullptr;
+  a.suffix_lens = nullptr;
+  a.part_ml = nullptr;
+  a.part_o = nullptr;
   hipError_t e =
       pa::launch_prefill(d->head_size, a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

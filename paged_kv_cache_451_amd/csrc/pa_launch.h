@@ -8,6 +8,9 @@
 
 namespace pa {
 
+// Key ranges per group of the shared-prefix pass of cascade decode.
+constexpr int kMaxSharedSplits = 16;
+
 // Everything one decode launch needs.
 struct DecodeArgs {
   const void* q;
@@ -28,6 +31,14 @@ struct DecodeArgs {
   void* v_pool_w;
   float* direct_ml;        // [B][Hq][2]
   float* direct_o;         // [B][Hq][D]
+  // Cascade decode: partials of the shared-prefix pass, one per (sequence,
+  // query head), folded in by the merge pass (null: no shared prefix), and
+  // the true lengths for the merge when seq_lens holds suffix lengths.
+  // (at most kMaxSharedSplits key ranges)
+  const float* shared_ml;  // [shared_splits][B][Hq][2]
+  const float* shared_o;   // [shared_splits][B][Hq][D]
+  int shared_splits;
+  const int32_t* full_lens;
   Sched s;
 };
 
@@ -84,21 +95,38 @@ struct PrefillSched {
   int NB;          // pool blocks
   int T;           // packed query rows (q_start[B])
   float c_log2;    // scale * log2(e)
+  int splits;      // shared-prefix pass: key ranges per group (else 1)
+  int attn_grid;   // workgroups of the attention part (set by the launcher)
 };
 struct PrefillArgs {
   const void* q;
   const void* k_pool;
   const void* v_pool;
   const int32_t* block_tables;
-  const int32_t* seq_lens;
-  const int32_t* q_start;
+  const int32_t* seq_lens;  // shared-prefix pass: prefix blocks per group
+  const int32_t* q_start;   // shared-prefix pass: group_start
   void* out;
+  // shared-prefix pass only: the decode batch's lengths and the partials
+  const int32_t* member_lens;  // [T]
+  float* part_ml;              // [splits][T][Hq][2]
+  float* part_o;               // [splits][T][Hq][D]
+  int32_t* suffix_tables;      // [T][max_blocks]: the suffix view
+  int32_t* suffix_lens;        // [T]
   PrefillSched s;
 };
 // Workgroups the prefill launch uses (an upper bound on the query tiles).
 int64_t prefill_grid(int head_size, int64_t T, int G, int B, int Hkv);
 hipError_t launch_prefill(int head_size, const PrefillArgs& a,
                           hipStream_t stream);
+// Shared-prefix pass of cascade decode (same kernel, s.B = groups, s.T =
+// decode sequences), s.splits key ranges per group: partials
+// [splits][T][Hq]; grid prefill_grid * splits, plus T workgroups that write
+// each sequence's suffix view: suffix_tables[b][k] = block_tables[b][k +
+// P_b] (-1 past the row), suffix_lens[b] = max(0, L_b - 16 P_b), where P_b
+// is the prefix blocks of b's group (0 outside every group); sequences
+// outside every group get empty partials (m = -inf, l = 0).
+hipError_t launch_shared_prefix(int head_size, const PrefillArgs& a,
+                                hipStream_t stream);
 
 // Copy-on-write block copy: K and V block src[i] -> dst[i] for every pair
 // (block_bytes per pool block, a multiple of 16).  Pairs with an id outside

@@ -35,6 +35,13 @@
 // causal mask is applied only on steps that reach past the smallest query
 // position of the wave.
 //
+// The same kernel runs the shared-prefix pass of cascade decode
+// (kShared): a "chunk" is then a group of consecutive decode sequences that
+// share their first P table entries, its query rows are the group's decode
+// queries, every row attends to all 16 P prefix keys before its own newest
+// token (no causal order inside the group), and the result is left as fp32
+// partials (running max, sum, unnormalised output) for the decode merge.
+//
 // Online softmax in base 2 with a lazily updated running max: the
 // accumulator is rescaled only when some row's max has grown by more than
 // 8 (log2 units) since the last rescale, so probabilities stay below 256.
@@ -94,15 +101,23 @@ struct Chunk {
   int qs, C, L;
 };
 
+// In the shared-prefix pass `seq_lens` holds each group's prefix blocks.
+template <bool kShared>
 __device__ __forceinline__ Chunk chunk_of(const int32_t* __restrict__ q_start,
                                           const int32_t* __restrict__ seq_lens,
                                           int b, const PrefillSched& sc) {
   int lo = q_start[b], hi = q_start[b + 1];
   lo = lo < 0 ? 0 : (lo > sc.T ? sc.T : lo);
   hi = hi < lo ? lo : (hi > sc.T ? sc.T : hi);
-  const int cap = sc.max_blocks * kBlock;
-  int L = seq_lens[b];
-  L = L < 0 ? 0 : (L > cap ? cap : L);
+  int L;
+  if (kShared) {
+    const int p = seq_lens[b];
+    L = (p < 0 ? 0 : (p > sc.max_blocks ? sc.max_blocks : p)) * kBlock;
+  } else {
+    const int cap = sc.max_blocks * kBlock;
+    L = seq_lens[b];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+  }
   return Chunk{lo, hi - lo, L};
 }
 
@@ -110,14 +125,17 @@ __device__ __forceinline__ Chunk chunk_of(const int32_t* __restrict__ q_start,
 // last row is min(C*G, (t+1)*COLS) - 1, its largest query position
 // L - C + that / G, and it takes ceil((position + 1) / 64) steps (0 when the
 // position is negative).  The step count does not decrease along t, so the
-// tiles taking >= W steps are a suffix.
+// tiles taking >= W steps are a suffix.  In the shared-prefix pass every
+// tile of a group takes ceil(L / 64) steps.
 __device__ __forceinline__ int tiles_of(const Chunk& c, int G) {
   return (c.C * G + kCols - 1) / kCols;
 }
 
+template <bool kShared>
 __device__ __forceinline__ int tiles_at_least(const Chunk& c, int G, int W) {
   const int nt = tiles_of(c, G);
   if (W <= 0) return nt;
+  if (kShared) return (c.L + kKeys - 1) / kKeys >= W ? nt : 0;
   // need position >= (W - 1) * 64, i.e. last row / G >= Y
   const int Y = (W - 1) * kKeys - (c.L - c.C);
   if (Y < 0) return nt;
@@ -134,6 +152,7 @@ __device__ __forceinline__ int wave_sum(int v) {
 }
 
 // Total over all sequences of tiles_at_least(W).
+template <bool kShared>
 __device__ __forceinline__ int count_at_least(
     const int32_t* __restrict__ q_start, const int32_t* __restrict__ seq_lens,
     const PrefillSched& sc, int W) {
@@ -142,31 +161,33 @@ __device__ __forceinline__ int count_at_least(
   for (int c0 = 0; c0 < sc.B; c0 += kWave) {
     const int b = c0 + lane;
     if (b < sc.B)
-      n += tiles_at_least(chunk_of(q_start, seq_lens, b, sc), sc.G, W);
+      n += tiles_at_least<kShared>(
+          chunk_of<kShared>(q_start, seq_lens, b, sc), sc.G, W);
   }
   return wave_sum(n);
 }
 
 // The r-th tile in order of decreasing step count: sequence b and tile t, or
 // b = -1 when r is past the last tile.  All arguments and results uniform.
+template <bool kShared>
 __device__ void tile_of_rank(const int32_t* __restrict__ q_start,
                              const int32_t* __restrict__ seq_lens,
                              const PrefillSched& sc, int r, int* b_out,
                              int* t_out) {
   *b_out = -1;
   *t_out = 0;
-  if (r >= count_at_least(q_start, seq_lens, sc, 0)) return;
+  if (r >= count_at_least<kShared>(q_start, seq_lens, sc, 0)) return;
   // largest W with count_at_least(W) > r
   int lo = 0, hi = (sc.max_blocks * kBlock + kKeys - 1) / kKeys + 1;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (count_at_least(q_start, seq_lens, sc, mid) > r)
+    if (count_at_least<kShared>(q_start, seq_lens, sc, mid) > r)
       lo = mid;
     else
       hi = mid;
   }
   const int W = lo;
-  const int k = r - count_at_least(q_start, seq_lens, sc, W + 1);
+  const int k = r - count_at_least<kShared>(q_start, seq_lens, sc, W + 1);
   // the k-th tile, in (sequence, tile) order, of those taking exactly W
   const int lane = lane_id();
   int carry = 0;
@@ -174,9 +195,9 @@ __device__ void tile_of_rank(const int32_t* __restrict__ q_start,
     const int b = c0 + lane;
     int eq = 0, first = 0;
     if (b < sc.B) {
-      const Chunk c = chunk_of(q_start, seq_lens, b, sc);
-      const int ge = tiles_at_least(c, sc.G, W);
-      eq = ge - tiles_at_least(c, sc.G, W + 1);
+      const Chunk c = chunk_of<kShared>(q_start, seq_lens, b, sc);
+      const int ge = tiles_at_least<kShared>(c, sc.G, W);
+      eq = ge - tiles_at_least<kShared>(c, sc.G, W + 1);
       first = tiles_of(c, sc.G) - ge;
     }
     const int incl = wave_incl_scan(eq) + carry;
@@ -191,19 +212,82 @@ __device__ void tile_of_rank(const int32_t* __restrict__ q_start,
   }
 }
 
-template <int D>
+__device__ __forceinline__ int clamp_to(int v, int hi) {
+  return v < 0 ? 0 : (v > hi ? hi : v);
+}
+
+// Group j of sequence b (group_start[j] <= b < group_start[j + 1], values
+// clamped to [0, B]), or -1.  A binary search over non-decreasing starts.
+__device__ int group_of(const int32_t* __restrict__ gs, int ng, int B, int b) {
+  int lo = 0, hi = ng - 1, j = -1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    if (clamp_to(gs[mid], B) <= b) {
+      j = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  if (j >= 0 && b >= clamp_to(gs[j + 1], B)) j = -1;
+  return j;
+}
+
+// Suffix view of sequence b of a cascade batch, for the decode main pass:
+// its table shifted left by its group's prefix blocks P (-1 past the row),
+// its length less 16 P; a sequence outside every group gets empty
+// shared-prefix partials (m = -inf, l = 0) in every key range.
+__device__ void suffix_row(int b, const int32_t* __restrict__ tables,
+                           const int32_t* __restrict__ lens,
+                           const int32_t* __restrict__ gs,
+                           const int32_t* __restrict__ gp,
+                           const PrefillSched& sc,
+                           int32_t* __restrict__ suffix_tables,
+                           int32_t* __restrict__ suffix_lens,
+                           float* __restrict__ part_ml) {
+  const int j = group_of(gs, sc.B, sc.T, b);
+  const int P = j >= 0 ? clamp_to(gp[j], sc.max_blocks) : 0;
+  const int32_t* row = tables + (size_t)b * sc.max_blocks;
+  int32_t* srow = suffix_tables + (size_t)b * sc.max_blocks;
+  for (int k = threadIdx.x; k < sc.max_blocks; k += kPfThreads)
+    srow[k] = k + P < sc.max_blocks ? row[k + P] : -1;
+  if (threadIdx.x == 0) {
+    const int L = clamp_to(lens[b], sc.max_blocks * kBlock);
+    const int Ls = L - P * kBlock;
+    suffix_lens[b] = Ls > 0 ? Ls : 0;
+  }
+  if (j < 0) {
+    for (int i = threadIdx.x; i < sc.Hq * sc.splits; i += kPfThreads) {
+      const int k = i / sc.Hq, hh = i - k * sc.Hq;
+      const size_t r = ((size_t)k * sc.T + b) * sc.Hq + hh;
+      part_ml[r * 2] = -INFINITY;
+      part_ml[r * 2 + 1] = 0.f;
+    }
+  }
+}
+
+template <int D, bool kShared>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k_pool,
     const __bf16* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ q_start, __bf16* __restrict__ out,
-    PrefillSched sc) {
+    const int32_t* __restrict__ member_lens, float* __restrict__ part_ml,
+    float* __restrict__ part_o, int32_t* __restrict__ suffix_tables,
+    int32_t* __restrict__ suffix_lens, PrefillSched sc) {
   typedef PfLds<D> Lay;
   constexpr int NK = D / 16;                  // 16-wide d chunks of Q^T
   constexpr int NX = D / 32;                  // 32-row d tiles of O^T
   __shared__ __attribute__((aligned(16))) uint8_t lds[Lay::Total];
 
+  // the shared-prefix launch ends with one workgroup per decode sequence
+  // that writes the sequence's suffix view
+  if (kShared && (int)blockIdx.x >= sc.attn_grid) {
+    suffix_row((int)blockIdx.x - sc.attn_grid, block_tables, member_lens,
+               q_start, seq_lens, sc, suffix_tables, suffix_lens, part_ml);
+    return;
+  }
   const int tid = threadIdx.x;
   __builtin_assume(tid < kPfThreads);
   const int wave = tid >> 6;
@@ -213,14 +297,28 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   const int g = blockIdx.x % sc.Hkv;
   const int G = sc.G;
 
+  // the shared-prefix pass also splits each group's keys into sc.splits
+  // ranges (adjacent workgroup ranks), so that few groups still fill the
+  // chip; each range leaves its own partial
+  const int r2 = blockIdx.x / sc.Hkv;
+  const int split = kShared ? r2 % sc.splits : 0;
   int b, t_in_b;
-  tile_of_rank(q_start, seq_lens, sc, blockIdx.x / sc.Hkv, &b, &t_in_b);
+  tile_of_rank<kShared>(q_start, seq_lens, sc, kShared ? r2 / sc.splits : r2,
+                        &b, &t_in_b);
   b = __builtin_amdgcn_readfirstlane(b);
   t_in_b = __builtin_amdgcn_readfirstlane(t_in_b);
   if (b < 0) return;
 
-  const Chunk ck = chunk_of(q_start, seq_lens, b, sc);
-  const int qs = ck.qs, C = ck.C, L = ck.L;
+  const Chunk ck = chunk_of<kShared>(q_start, seq_lens, b, sc);
+  const int qs = ck.qs, C = ck.C;
+  // keys the pass may read: the chunk's context; in the shared-prefix pass
+  // the prefix, cut at the first member's tokens before its newest (the
+  // rows it reads through), so that no unwritten slot enters a product
+  int L = ck.L;
+  if (kShared) {
+    const int lf = member_lens[qs] - 1;
+    L = lf < 0 ? 0 : (lf < L ? lf : L);
+  }
   const int rows_b = C * G;
   const int row0 = t_in_b * kCols;
   const int nblk = (L + kBlock - 1) / kBlock;
@@ -230,7 +328,16 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   const bool row_ok = row < rows_b;
   const int ti = row_ok ? row / G : 0;
   const int hn = row_ok ? row - ti * G : 0;
-  const int pos = row_ok ? L - C + ti : -1;
+  // largest key position the row attends: causal within a prefill chunk;
+  // in the shared-prefix pass every prefix key before the sequence's newest
+  // token (which the merge adds)
+  int pos;
+  if (kShared) {
+    const int lm = member_lens[qs + ti] - 1;  // keys before the newest
+    pos = row_ok ? (lm < L ? lm : L) - 1 : -1;
+  } else {
+    pos = row_ok ? L - C + ti : -1;
+  }
   bf16x8 qb[NK];
   {
     const __bf16* qrow =
@@ -246,10 +353,29 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     }
   }
   const int last_row = (rows_b < row0 + kCols ? rows_b : row0 + kCols) - 1;
-  const int p_max = L - C + last_row / G;  // largest query position
-  const int wp_min = L - C + (row0 + kRows * wave) / G;  // smallest, wave
-  const int kend = p_max + 1 < L ? p_max + 1 : L;        // keys needed
+  int wp_min, kend;  // smallest position of the wave; keys needed
+  if (kShared) {
+    int v = row_ok ? pos : INT32_MAX;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_xor(v, o, kWave);
+      v = t < v ? t : v;
+    }
+    wp_min = v;
+    kend = L;
+  } else {
+    const int p_max = L - C + last_row / G;  // largest query position
+    wp_min = L - C + (row0 + kRows * wave) / G;
+    kend = p_max + 1 < L ? p_max + 1 : L;
+  }
   const int nsteps = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
+  // steps [s_begin, s_end) of this workgroup
+  int s_begin = 0, s_end = nsteps;
+  if (kShared) {
+    const int per = (nsteps + sc.splits - 1) / sc.splits;
+    s_begin = split * per < nsteps ? split * per : nsteps;
+    s_end = s_begin + per < nsteps ? s_begin + per : nsteps;
+  }
 
   f32x16 acc[NX];
 #pragma unroll
@@ -258,7 +384,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     for (int i = 0; i < 16; ++i) acc[X][i] = 0.f;
   float m_run = -INFINITY, lsum = 0.f;
 
-  const int32_t* trow = block_tables + (size_t)b * sc.max_blocks;
+  // the group's prefix is read through its first member's table row
+  const int32_t* trow =
+      block_tables + (size_t)(kShared ? qs : b) * sc.max_blocks;
 
   // Block ids: lane u % 4 holds the entry of block 4 s + u % 4 of a step.
   // They are loaded two steps ahead, so the K/V loads never wait on them.
@@ -362,21 +490,22 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   // all of them before the first product.
   int nv_cur[4] = {0, 0, 0, 0};
   int ids_next = 0;  // table entries of the next load
-  const int last = nsteps - 1;
-  if (nsteps > 0) {
-    const int e0 = table_entry(0);
+  const int last = s_end - 1;
+  if (s_end > s_begin) {
+    const int e0 = table_entry(s_begin);
     u32x4 rk[VPT], rv[VPT];
     load_tiles(kp, e0, rk);
     load_tiles(vp, e0, rv);
-    valid_of(0, e0, nv_cur);
-    ids_next = table_entry(last < 1 ? last : 1);
+    valid_of(s_begin, e0, nv_cur);
+    ids_next = table_entry(last < s_begin + 1 ? last : s_begin + 1);
     store_k(0, rk);
     store_v(0, rv, nv_cur);
   }
   __syncthreads();
 
-  for (int s = 0; s < nsteps; ++s) {
+  for (int s = s_begin; s < s_end; ++s) {
     const bool more = s < last;
+    const int buf = (s - s_begin) & 1;
     u32x4 rk[VPT], rv[VPT];
     int nv_next[4];
     load_tiles(kp, ids_next, rk);  // step min(s + 1, last)
@@ -385,7 +514,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     ids_next = table_entry(s + 2 < last ? s + 2 : last);
 
     f32x16 s_cur[2];
-    scores(s & 1, s_cur);
+    scores(buf, s_cur);
     const int key0 = s * kKeys;
     const bool full = nv_cur[0] == kBlock && nv_cur[1] == kBlock &&
                       nv_cur[2] == kBlock && nv_cur[3] == kBlock &&
@@ -440,7 +569,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
           const bf16x2 pp = {p0, p1};
           lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
         }
-    const uint8_t* vbase = lds + (s & 1) * Lay::VBytes + v_off;
+    const uint8_t* vbase = lds + buf * Lay::VBytes + v_off;
 #pragma unroll
     for (int X = 0; X < NX; ++X)
 #pragma unroll
@@ -451,8 +580,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
               vbase + X * 32 * Lay::VRow + (32 * hf + 16 * c) * 2);
           acc[X] = mfma32(va, pb[hf][c], acc[X]);
         }
-    store_k((s + 1) & 1, rk);
-    store_v((s + 1) & 1, rv, nv_next);
+    store_k(buf ^ 1, rk);
+    store_v(buf ^ 1, rv, nv_next);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 4; ++u) nv_cur[u] = nv_next[u];
@@ -460,6 +589,26 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
 
   // lane (n, h) holds O[row n][32 X + 8 a + 4 h + i] in element 4 a + i
   const float ltot = lsum + __shfl_xor(lsum, 32, kWave);
+  if (kShared) {
+    if (row_ok) {
+      const size_t hrow =
+          ((size_t)split * sc.T + qs + ti) * sc.Hq + (size_t)g * G + hn;
+      if (h == 0) {
+        part_ml[hrow * 2] = m_run;
+        part_ml[hrow * 2 + 1] = ltot;
+      }
+      float* orow = part_o + hrow * D + 4 * h;
+#pragma unroll
+      for (int X = 0; X < NX; ++X)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float4 o = {acc[X][4 * a], acc[X][4 * a + 1],
+                            acc[X][4 * a + 2], acc[X][4 * a + 3]};
+          *reinterpret_cast<float4*>(orow + 32 * X + 8 * a) = o;
+        }
+    }
+    return;
+  }
   if (row_ok) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     __bf16* orow =
@@ -476,17 +625,22 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   }
 }
 
-template <int D>
+template <int D, bool kShared>
 void launch_pf(const PrefillArgs& a, hipStream_t stream) {
   const int tiles =
       (int)(((int64_t)a.s.T * a.s.G + kCols - 1) / kCols) + a.s.B;
-  hipLaunchKernelGGL((prefill_mfma_kernel<D>),
-                     dim3((unsigned)(tiles * a.s.Hkv)), dim3(kPfThreads), 0,
+  const int splits = kShared ? a.s.splits : 1;
+  PrefillSched s = a.s;
+  s.attn_grid = tiles * a.s.Hkv * splits;
+  const int grid = s.attn_grid + (kShared ? a.s.T : 0);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, kShared>), dim3((unsigned)grid),
+                     dim3(kPfThreads), 0,
                      stream, reinterpret_cast<const __bf16*>(a.q),
                      reinterpret_cast<const __bf16*>(a.k_pool),
                      reinterpret_cast<const __bf16*>(a.v_pool), a.block_tables,
                      a.seq_lens, a.q_start, reinterpret_cast<__bf16*>(a.out),
-                     a.s);
+                     a.member_lens, a.part_ml, a.part_o, a.suffix_tables,
+                     a.suffix_lens, s);
 }
 
 }  // namespace
@@ -500,8 +654,19 @@ hipError_t launch_prefill(int head_size, const PrefillArgs& a,
                           hipStream_t stream) {
   if (a.s.B == 0 || a.s.T == 0) return hipSuccess;
   switch (head_size) {
-    case 64: launch_pf<64>(a, stream); break;
-    case 128: launch_pf<128>(a, stream); break;
+    case 64: launch_pf<64, false>(a, stream); break;
+    case 128: launch_pf<128, false>(a, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_prefix(int head_size, const PrefillArgs& a,
+                                hipStream_t stream) {
+  if (a.s.B == 0 || a.s.T == 0) return hipSuccess;
+  switch (head_size) {
+    case 64: launch_pf<64, true>(a, stream); break;
+    case 128: launch_pf<128, true>(a, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -132,6 +132,37 @@ def test_fused_step_checks_its_extra_pointers(lib):
                                 ctypes.byref(e), None, 0, None) == 0
 
 
+def test_shared_prefix_step_checks(lib):
+    p, odd = ctypes.c_void_p(256), ctypes.c_void_p(258)
+    f = lib.pa_decode_append_shared
+
+    def call(desc, gs=p, gp=p, ng=1, scale=1.0, kn=p):
+        return f(p, p, p, p, p, ctypes.c_float(scale), p, kn, p, p, gs, gp,
+                 ng, ctypes.byref(desc), p, 1 << 20, None)
+
+    assert call(_desc(kv_dtype=_lib.PA_FP8_E4M3FN)) == -2
+    assert call(_desc(q_dtype=_lib.PA_F32, kv_dtype=_lib.PA_F32,
+                      num_q_heads=4)) == -2
+    assert call(_desc(head_size=256)) == -3
+    assert call(_desc(num_q_heads=7)) == -3
+    assert call(_desc(), ng=3) == -3          # more groups than sequences
+    assert call(_desc(), ng=-1) == -3
+    assert call(_desc(), scale=0.0) == -3
+    assert call(_desc(), scale=float("nan")) == -3
+    assert call(_desc(), gs=None) == -1
+    assert call(_desc(), gp=None) == -1
+    assert call(_desc(), gs=odd) == -4
+    assert call(_desc(), gp=odd) == -4
+    assert call(_desc(), kn=None) == -1
+    assert f(p, p, p, p, p, ctypes.c_float(1.0), p, p, p, p, p, p, 1, None,
+             p, 1 << 20, None) == -1
+    assert lib.pa_decode_append_shared_workspace_size(
+        ctypes.byref(_desc(num_q_heads=7))) == 0
+    e = _desc(num_seqs=0)
+    assert f(None, None, None, None, None, ctypes.c_float(1.0), None, None,
+             None, None, None, None, 0, ctypes.byref(e), None, 0, None) == 0
+
+
 def test_null_pointers_and_alignment_are_rejected(lib):
     assert lib.pa_decode(None, None, None, None, None, ctypes.c_float(1.0),
                          None, None, None, 0, None) == -1
