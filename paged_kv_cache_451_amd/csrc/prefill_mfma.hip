@@ -467,18 +467,27 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   const int k_off = n32 * Lay::KRow + 16 * h;
   const int v_off = Lay::V0 + n32 * Lay::VRow + 16 * h;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // The two halves' products alternate (independent accumulators back to
+  // back), and the K fragments are read kAhead products ahead.
+  constexpr int kAhead = 4;
   auto scores = [&](int kbuf, f32x16 sv[2]) {
     const uint8_t* base = lds + kbuf * Lay::KBytes + k_off;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[hf][i] = 0.f;
+    auto frag = [&](int t) {  // product t: d chunk t / 2, half t % 2
+      return *reinterpret_cast<const bf16x8*>(base + (t & 1) * 32 * Lay::KRow +
+                                              32 * (t >> 1));
+    };
+    bf16x8 ring[kAhead];
 #pragma unroll
-      for (int c = 0; c < NK; ++c) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-            base + hf * 32 * Lay::KRow + 32 * c);
-        sv[hf] = mfma32(ka, qb[c], sv[hf]);
-      }
+    for (int t = 0; t < kAhead; ++t) ring[t] = frag(t);
+#pragma unroll
+    for (int t = 0; t < 2 * NK; ++t) {
+      const bf16x8 ka = ring[t % kAhead];
+      if (t + kAhead < 2 * NK) ring[t % kAhead] = frag(t + kAhead);
+      sv[t & 1] = mfma32(ka, qb[t >> 1], sv[t & 1]);
     }
   };
 
@@ -569,17 +578,24 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
           const bf16x2 pp = {p0, p1};
           lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
         }
+    // products: 16-key chunk outer, d tile inner (independent
+    // accumulators back to back), V fragments read kAhead ahead
     const uint8_t* vbase = lds + buf * Lay::VBytes + v_off;
+    auto vfrag = [&](int t) {  // product t: chunk t / NX, d tile t % NX
+      const int ch = t / NX, X = t % NX;
+      return *reinterpret_cast<const bf16x8*>(vbase + X * 32 * Lay::VRow +
+                                              ch * 32);
+    };
+    bf16x8 vring[kAhead];
 #pragma unroll
-    for (int X = 0; X < NX; ++X)
+    for (int t = 0; t < kAhead; ++t) vring[t] = vfrag(t);
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-              vbase + X * 32 * Lay::VRow + (32 * hf + 16 * c) * 2);
-          acc[X] = mfma32(va, pb[hf][c], acc[X]);
-        }
+    for (int t = 0; t < 4 * NX; ++t) {
+      const bf16x8 va = vring[t % kAhead];
+      if (t + kAhead < 4 * NX) vring[t % kAhead] = vfrag(t + kAhead);
+      const int ch = t / NX;
+      acc[t % NX] = mfma32(va, pb[ch >> 1][ch & 1], acc[t % NX]);
+    }
     store_k(buf ^ 1, rk);
     store_v(buf ^ 1, rv, nv_next);
     __syncthreads();
