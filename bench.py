@@ -631,25 +631,15 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / a.steps
 
-    # the dominant kernel alone: HIP events recorded on the launch stream
-    # right before and after each main decode kernel (events serialise the
-    # stream, so this runs as its own region after the timed one)
-    if cascade:
-        # four launches share the work: time the whole step with events
-        # around each call on the launch stream
-        roof = [prepared(i, base_desc) for i in range(len(ev))]
-        for step, (e0, e1) in zip(roof, ev):
-            e0.record(stream)
-            step()
-            e1.record(stream)
-    else:
-        roof = [_lib.PreparedStep(q, kps[i % nrot], vps[i % nrot], tables,
-                                  lens, case.scale, out,
-                                  desc_for((e0.cuda_event, e1.cuda_event)),
-                                  ws, k_new, v_new, slots, fused=fused)
-                for i, (e0, e1) in enumerate(ev)]
-        for step in roof:
-            step()
+    # The dominant kernel's duration: the same steps again, each recording a
+    # pair of HIP events on the launch stream around its main kernel (around
+    # all its launches for the cascade step).  Timing events serialise the
+    # stream - on MI355X they cost about 6 us per step - so they run as a
+    # region of their own after the timed one.
+    roof = [prepared(i, desc_for((e0.cuda_event, e1.cuda_event)))
+            for i, (e0, e1) in enumerate(ev)]
+    for step in roof:
+        step()
     torch.cuda.synchronize()
     kern_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     kern_ms.sort()

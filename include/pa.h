@@ -101,7 +101,9 @@ typedef enum {
  *                       workgroups of the main kernel (rounded to a multiple
  *                       of num_kv_heads).
  *   profile_events      NULL, or two hipEvent_t the call records on `stream`
- *                       immediately before and after the main kernel.
+ *                       immediately before and after the main kernel (for
+ *                       pa_decode_append_shared with groups: before its
+ *                       first and after its last launch).
  */
 typedef struct {
   int32_t num_seqs;

@@ -258,7 +258,13 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
   a.full_lens = nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (sp && sp->num_groups > 0) {
+  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(
+      const_cast<void**>(desc->profile_events));
+  // the cascade step's events bracket all of its launches
+  const bool cascade = sp && sp->num_groups > 0;
+  if (cascade && ev[0] && hipEventRecord(ev[0], s) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  if (cascade) {
     // one launch reads the shared prefixes once per group and writes the
     // suffix view of every sequence; the main and merge passes below run
     // on the suffixes
@@ -298,9 +304,8 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
     a.shared_o = so;
     a.shared_splits = p.splits;
   }
-  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(
-      const_cast<void**>(desc->profile_events));
-  if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return PA_ERR_LAUNCH;
+  if (!cascade && ev[0] && hipEventRecord(ev[0], s) != hipSuccess)
+    return PA_ERR_LAUNCH;
   hipError_t e;
   if (desc->kv_dtype == PA_F32)
     e = pa::launch_decode_valu(desc->head_size, a, p.W, s);
@@ -308,14 +313,18 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
     e = pa::launch_decode_mfma(desc->kv_dtype == PA_FP8_E4M3FN,
                                desc->head_size, a, p.W, s);
   if (e != hipSuccess) return PA_ERR_LAUNCH;
-  if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return PA_ERR_LAUNCH;
+  if (!cascade && ev[1] && hipEventRecord(ev[1], s) != hipSuccess)
+    return PA_ERR_LAUNCH;
   if (fused)
     e = pa::launch_decode_merge_append((int)dtype_bytes(desc->kv_dtype),
                                        desc->head_size, a, s);
   else
     e = pa::launch_decode_merge(desc->q_dtype == PA_BF16, desc->head_size, a,
                                 s);
-  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  if (cascade && ev[1] && hipEventRecord(ev[1], s) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
 }
 
 }  // namespace
