@@ -265,3 +265,49 @@ def test_empty_calls_are_no_ops(lib):
                         block_size=16, num_blocks=4, kv_dtype=_lib.PA_BF16)
     assert lib.pa_kv_append(None, None, None, None, None, ctypes.byref(a),
                             None) == 0
+
+
+def test_a_plain_c_program_links_and_calls_the_library(lib):
+    """The header and library used from C alone (gcc, no Python binding):
+    every declared function links, and host-side checks answer without a
+    device."""
+    src = r'''
+#include <stdio.h>
+#include <string.h>
+#include "pa.h"
+int main(void) {
+  if (pa_abi_version() != %d) return 1;
+  if (strcmp(pa_status_string(PA_OK), "success") != 0) return 2;
+  pa_decode_desc d;
+  memset(&d, 0, sizeof d);
+  d.num_seqs = 1; d.num_q_heads = 4; d.num_kv_heads = 2; d.head_size = 96;
+  d.block_size = 16; d.num_blocks = 4; d.max_blocks_per_seq = 2;
+  d.q_dtype = PA_BF16; d.kv_dtype = PA_BF16; d.k_scale = d.v_scale = 1.f;
+  if (pa_decode_workspace_size(&d) != 0) return 3;     /* head_size 96 */
+  if (pa_decode(0, 0, 0, 0, 0, 1.f, 0, &d, 0, 0, 0) != PA_ERR_SHAPE) return 4;
+  pa_append_desc a;
+  memset(&a, 0, sizeof a);
+  a.num_tokens = 0; a.num_kv_heads = 2; a.head_size = 64; a.block_size = 16;
+  a.num_blocks = 4; a.kv_dtype = PA_BF16;
+  if (pa_kv_append(0, 0, 0, 0, 0, &a, 0) != PA_OK) return 5; /* no tokens */
+  /* every other entry point links */
+  void* fns[] = {(void*)pa_decode_append, (void*)pa_decode_append_shared,
+                 (void*)pa_kv_append_quant, (void*)pa_copy_blocks,
+                 (void*)pa_prefill, (void*)pa_decode_append_workspace_size,
+                 (void*)pa_decode_append_shared_workspace_size};
+  for (unsigned i = 0; i < sizeof fns / sizeof fns[0]; ++i)
+    if (!fns[i]) return 6;
+  printf("ok\n");
+  return 0;
+}
+''' % lib.pa_abi_version()
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(c, "w").write(src)
+        libdir = os.path.dirname(_lib.LIB_PATH)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"),
+                        c, "-o", exe, "-L", libdir, "-lpa",
+                        f"-Wl,-rpath,{libdir}"], check=True)
+        r = subprocess.run([exe], capture_output=True, text=True)
+        assert r.returncode == 0 and r.stdout.strip() == "ok", \
+            (r.returncode, r.stdout, r.stderr)
