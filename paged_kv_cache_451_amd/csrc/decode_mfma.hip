@@ -193,6 +193,22 @@ struct Pair<true, D> {
   }
 };
 
+// One sequence b of a workgroup's range: the part [lo, hi) of its blocks
+// that the range covers, its pool length L, and which partial slot it
+// leaves (-1: the range holds all of it, 0: it started in an earlier range,
+// 1: it continues in a later one).
+struct Seg {
+  int b, lo, hi, L, slot;
+  __device__ __forceinline__ void bind(const int32_t* __restrict__ lens,
+                                       const Sched& sc, int Sb, int Sb1,
+                                       int u0, int u1) {
+    lo = (Sb > u0 ? Sb : u0) - Sb;
+    hi = (Sb1 < u1 ? Sb1 : u1) - Sb;
+    L = pool_len(lens[b], sc.len_bias, sc.max_blocks);
+    slot = Sb < u0 ? 0 : (Sb1 > u1 ? 1 : -1);
+  }
+};
+
 // Minimum resident waves per SIMD the register budget is held to.
 template <int D>
 constexpr int min_waves() { return D > 128 ? 1 : 2; }
@@ -235,53 +251,81 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
   const bool k_hi = r16 >= 8;  // K row from the pair's second block
   const bool v_hi = j >= 2;    // V tokens from the pair's second block
 
-  for_each_segment(seq_lens, sc.B, sc.max_blocks, sc.len_bias, u0, u1,
-                   [&](int b, int Sb, int Sb1) {
-    const int L = pool_len(seq_lens[b], sc.len_bias, sc.max_blocks);
-    const int lo = (Sb > u0 ? Sb : u0) - Sb;
-    const int hi = (Sb1 < u1 ? Sb1 : u1) - Sb;
-    const int32_t* trow = block_tables + (size_t)b * sc.max_blocks;
+  // The range's sequences ("segments") in order, one ahead of the one being
+  // computed: the last loads a segment issues are the next segment's first
+  // pair, so the wave's stream of loads does not stop between sequences.
+  SegCursor cursor(seq_lens, sc.B, sc.max_blocks, sc.len_bias, u0, u1);
+  Seg cur, nxt;
+  int Sb, Sb1;
+  if (!cursor.next(cur.b, Sb, Sb1)) return;
+  cur.bind(seq_lens, sc, Sb, Sb1, u0, u1);
+  bool more = cursor.next(nxt.b, Sb, Sb1);
+  if (more) nxt.bind(seq_lens, sc, Sb, Sb1, u0, u1);
+  // block-table row of sequence b
+  auto trow = [&](int b) { return block_tables + (size_t)b * sc.max_blocks; };
 
-    // Loads of the pair starting at block pblk.  A pair at or past the end
-    // of the segment is never computed; its loads go to this sequence's q
-    // row (a few lines that are cached anyway) instead of HBM.
+  // Q as the B operand of QK: lane (n, j) holds head g*G + n.
+  auto load_q = [&](bf16x8* qv, int b) {
+    const int n = r16;
+    const __bf16* qrow = q + ((size_t)b * sc.Hq + (size_t)g * G + n) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 z = {};
+      qv[c] = n < G ? *reinterpret_cast<const bf16x8*>(qrow + P::qcol(c, j))
+                    : z;
+    }
+  };
+
+  P A, B;
+  // Table entries of the pairs ahead (see the loop invariant below).
+  RawIds ia = raw_ids(trow(cur.b), cur.lo, cur.hi);
+  RawIds ib, ic, id;
+  // Loads of pair pblk of the current segment, or, at and past its loop
+  // end `blk_end`, of the next segment's pair at nxt.lo + (pblk - blk_end).
+  // A pair past both is never computed: its loads go to the current
+  // sequence's q row (a few lines that are cached anyway) instead of HBM.
+  auto issue = [&](P& pr, const RawIds& ids, int pblk, const Seg& s,
+                   int blk_end) {
+    const size_t base0 = (size_t)safe_id(ids.e0, sc.NB) * btile + gtile;
+    const size_t base1 = (size_t)safe_id(ids.e1, sc.NB) * btile + gtile;
+    const bool live =
+        pblk < s.hi ||
+        (more && pblk >= blk_end && nxt.lo + (pblk - blk_end) < nxt.hi);
     const T* q_as_t = reinterpret_cast<const T*>(
-        q + ((size_t)b * sc.Hq + (size_t)g * G) * D);
-    auto issue = [&](P& pr, const RawIds& id, int pblk) {
-      const size_t base0 = (size_t)safe_id(id.e0, sc.NB) * btile + gtile;
-      const size_t base1 = (size_t)safe_id(id.e1, sc.NB) * btile + gtile;
-      const bool live = pblk < hi;
-      pr.load(live ? kpool + (k_hi ? base1 : base0) + k_lane : q_as_t,
-              live ? vpool + (v_hi ? base1 : base0) + v_lane : q_as_t);
+        q + ((size_t)s.b * sc.Hq + (size_t)g * G) * D);
+    pr.load(live ? kpool + (k_hi ? base1 : base0) + k_lane : q_as_t,
+            live ? vpool + (v_hi ? base1 : base0) + v_lane : q_as_t);
+  };
+  issue(A, ia, cur.lo, cur, cur.lo + 4);
+  ib = raw_ids(trow(cur.b), cur.lo + 2, cur.hi);
+
+  bf16x8 qb[NC], qn[NC];
+  load_q(qb, cur.b);
+
+  f32x4 acc[NX];
+  float m, lsum;
+
+  for (;;) {  // segments
+    // first pair index the pair loop below does not compute
+    const int blk_end = cur.lo + 4 * ((cur.hi - cur.lo + 3) >> 2);
+    const int L = cur.L;
+    const int hi = cur.hi;
+    if (more) load_q(qn, nxt.b);
+    auto ids_at = [&](int pblk) {
+      const bool here = pblk < blk_end || !more;
+      return raw_ids(trow(here ? cur.b : nxt.b),
+                     here ? pblk : nxt.lo + (pblk - blk_end),
+                     here ? hi : nxt.hi);
     };
 
-    RawIds ia = raw_ids(trow, lo, hi);
-    P A, B;
-    issue(A, ia, lo);
-    RawIds ib = raw_ids(trow, lo + 2, hi);
-
-    // Q as the B operand of QK: lane (n, j) holds head g*G + n.
-    bf16x8 qb[NC];
-    {
-      const int n = r16;
-      const __bf16* qrow = q + ((size_t)b * sc.Hq + (size_t)g * G + n) * D;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        bf16x8 z = {};
-        qb[c] = n < G ? *reinterpret_cast<const bf16x8*>(qrow + P::qcol(c, j))
-                      : z;
-      }
-    }
-
-    f32x4 acc[NX];
 #pragma unroll
     for (int x = 0; x < NX; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY;
-    float lsum = 0.f;
+    m = -INFINITY;
+    lsum = 0.f;
 
-    auto compute = [&](const P& pr, const RawIds& id, int blk) {
+    auto compute = [&](const P& pr, const RawIds& ids, int blk) {
       int nv0, nv1;
-      pair_valid(id, blk, hi, L, sc.NB, nv0, nv1);
+      pair_valid(ids, blk, hi, L, sc.NB, nv0, nv1);
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -331,21 +375,22 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
       }
     };
 
-    // Loop invariant: A holds the loads of pair blk, ib the table entries of
-    // pair blk + 2.  Loads are issued unconditionally (see raw_ids), and the
-    // loop leaves only after computing both register sets: when a segment
-    // has an odd number of pairs, the last B pair lies past its end and is
-    // computed with every token masked.  A loop exit with one set's loads
-    // still outstanding would make the compiler wait for all loads at the
-    // top of every iteration of the next segment.
-    int blk = lo;
+    // Loop invariant: A holds the loads of pair blk, ia its table entries,
+    // ib the entries of pair blk + 2.  Loads are issued unconditionally
+    // (see raw_ids), and the loop leaves only after computing both register
+    // sets: when a segment has an odd number of pairs, the last B pair lies
+    // past its end and is computed with every token masked.  The loop
+    // leaves with A holding the next segment's first pair, the same state
+    // as at its back edge, so the compiler's wait before each pair's math
+    // leaves the following pair's loads outstanding.
+    int blk = cur.lo;
     for (;;) {
-      issue(B, ib, blk + 2);
-      RawIds ic = raw_ids(trow, blk + 4, hi);
+      issue(B, ib, blk + 2, cur, blk_end);
+      ic = ids_at(blk + 4);
       compute(A, ia, blk);
       blk += 2;
-      issue(A, ic, blk + 2);
-      RawIds id = raw_ids(trow, blk + 4, hi);
+      issue(A, ic, blk + 2, cur, blk_end);
+      id = ids_at(blk + 4);
       compute(B, ib, blk);
       blk += 2;
       if (blk >= hi) break;
@@ -357,8 +402,9 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
     float ltot = lsum + __shfl_xor(lsum, 16, kWave);
     ltot += __shfl_xor(ltot, 32, kWave);
     const int n = r16;
+    const int b = cur.b;
     if (n < G) {
-      const bool split = Sb < u0 || Sb1 > u1;
+      const bool split = cur.slot >= 0;
       if (!split && sc.len_bias) {
         // the merge pass still has to fold in the appended token
         const size_t row = (size_t)b * sc.Hq + (size_t)g * G + n;
@@ -382,8 +428,7 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
           *reinterpret_cast<bf16x4*>(orow + 16 * xx) = o;
         }
       } else {
-        const int slot = Sb < u0 ? 0 : 1;
-        const size_t row = ((size_t)w * 2 + slot) * G + n;
+        const size_t row = ((size_t)w * 2 + cur.slot) * G + n;
         float* po = part_o + row * D + 4 * j;
 #pragma unroll
         for (int xx = 0; xx < NX; ++xx)
@@ -394,7 +439,16 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
         }
       }
     }
-  });
+
+    if (!more) break;
+    cur = nxt;
+    more = cursor.next(nxt.b, Sb, Sb1);
+    if (more) nxt.bind(seq_lens, sc, Sb, Sb1, u0, u1);
+    ia = ic;
+    ib = id;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qb[c] = qn[c];
+  }
 }
 
 template <bool FP8, int D>

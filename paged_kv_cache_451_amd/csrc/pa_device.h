@@ -126,6 +126,53 @@ __device__ inline void for_each_segment(const int32_t* __restrict__ seq_lens,
   }
 }
 
+// The same walk as for_each_segment, one segment per call, so that a kernel
+// can look one segment ahead.  All state is uniform.
+struct SegCursor {
+  const int32_t* __restrict__ seq_lens;
+  int B, max_blocks, bias, u0, u1;
+  int c0;          // first sequence of the scanned chunk of kWave sequences
+  int chunk_end;   // blocks before the next chunk
+  int excl, incl;  // per lane: block span of sequence c0 + lane
+  uint64_t mask;   // lanes of the chunk still to visit
+  bool last;       // no later chunk can overlap [u0, u1)
+
+  __device__ SegCursor(const int32_t* __restrict__ lens, int B_, int mb,
+                       int bias_, int u0_, int u1_)
+      : seq_lens(lens), B(B_), max_blocks(mb), bias(bias_), u0(u0_),
+        u1(u1_), c0(0), chunk_end(0) {
+    scan();
+  }
+
+  __device__ void scan() {
+    const int b = c0 + lane_id();
+    const int nb =
+        b < B ? (pool_len(seq_lens[b], bias, max_blocks) + kBlock - 1) / kBlock
+              : 0;
+    incl = wave_incl_scan(nb) + chunk_end;
+    excl = incl - nb;
+    chunk_end = readlane(incl, kWave - 1);
+    const uint64_t m = __ballot(nb > 0 && excl < u1 && incl > u0);
+    mask = chunk_end > u0 ? m : 0;
+    last = chunk_end >= u1 || c0 + kWave >= B;
+  }
+
+  // Next sequence b whose non-empty span [Sb, Sb1) overlaps [u0, u1).
+  __device__ bool next(int& b, int& Sb, int& Sb1) {
+    while (!mask) {
+      if (last) return false;
+      c0 += kWave;
+      scan();
+    }
+    const int i = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    b = c0 + i;
+    Sb = readlane(excl, i);
+    Sb1 = readlane(incl, i);
+    return true;
+  }
+};
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
