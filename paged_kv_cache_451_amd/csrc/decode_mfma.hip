@@ -383,13 +383,18 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
     // leaves with A holding the next segment's first pair, the same state
     // as at its back edge, so the compiler's wait before each pair's math
     // leaves the following pair's loads outstanding.
+    // The scheduling barriers keep each pair's loads issued before the
+    // other pair's math: left free, the scheduler may sink them below it,
+    // which leaves a pair's loads no time in flight.
     int blk = cur.lo;
     for (;;) {
       issue(B, ib, blk + 2, cur, blk_end);
+      __builtin_amdgcn_sched_barrier(0);
       ic = ids_at(blk + 4);
       compute(A, ia, blk);
       blk += 2;
       issue(A, ic, blk + 2, cur, blk_end);
+      __builtin_amdgcn_sched_barrier(0);
       id = ids_at(blk + 4);
       compute(B, ib, blk);
       blk += 2;
