@@ -256,6 +256,9 @@ EDGE = [
     dict(lens=[64, 5, 129], hq=4, hkv=4, d=128),           # G = 1 on MFMA
     dict(lens=[200, 33], hq=6, hkv=2, d=256),              # D = 256, G = 3
     dict(lens=[100, 17], hq=4, hkv=2, d=64, kv_dtype="fp8_e4m3fn"),
+    dict(lens=[90, 300], hq=8, hkv=2, d=256, kv_dtype="fp8_e4m3fn"),
+    dict(lens=[33, 1, 250], hq=16, hkv=1, d=128,
+         kv_dtype="fp8_e4m3fn"),                            # fp8, G = 16
     dict(lens=[1, 16, 77], hq=8, hkv=1, d=128, q_dtype="f32",
          kv_dtype="f32"),                                   # fp32, G = 8
     dict(lens=[1, 40], hq=2, hkv=2, d=256, q_dtype="f32", kv_dtype="f32"),
