@@ -28,12 +28,14 @@
 //
 // K/V go through LDS: each step the workgroup copies the four 16-token K
 // tiles ([16][D] each) and V tiles ([D][16] each) of KV head g into one of
-// two LDS buffers while the waves compute on the other.  Rows are padded by
-// 16 bytes so the 16-byte operand reads of a wave spread over the banks.
-// Keys at or past the sequence end, or in blocks with an out-of-range id,
-// get zero V (a masked probability times them is 0) and a -inf score.  The
-// causal mask is applied only on steps that reach past the smallest query
-// position of the wave.
+// two LDS buffers while the waves compute on the other.  The copies go from
+// the pool straight into LDS (no registers on the way), wave w copying
+// block w of the step; unpadded rows with XOR-swizzled 16-byte chunks keep
+// the operand reads free of bank conflicts.  Keys at or past the sequence
+// end, or in blocks with an out-of-range id, get a -inf score, and their V
+// is zeroed in LDS after the copy lands (a masked probability times them
+// must be 0 even where the slot holds NaN).  The causal mask is applied only
+// on steps that reach past the smallest query position of the wave.
 //
 // The same kernel runs the shared-prefix pass of cascade decode
 // (kShared): a "chunk" is then a group of consecutive decode sequences that
@@ -58,6 +60,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kPfWaves = kPrefillWaves;
 constexpr int kPfThreads = kPfWaves * kWave;
@@ -66,15 +69,43 @@ constexpr int kCols = kPfWaves * kRows;  // query rows per workgroup
 constexpr int kKeys = 64;                // keys per step: four blocks
 constexpr float kLazy = 8.0f;            // rescale threshold (log2 units)
 
+// LDS of one workgroup: two K buffers then two V buffers.  A K buffer holds
+// a step's 64 key rows of D values (row k_lds_row(key)), a V buffer the
+// step's four [D][16] V tiles back to back.  Rows are not padded: the
+// 16-byte chunks of K row r sit at position chunk ^ kswz(r), those of V row
+// d at half ^ ((d >> 3) & 1), which spreads every 16-lane group of operand
+// reads over all banks.
 template <int D>
 struct PfLds {
-  static constexpr int KRow = D * 2 + 16;      // bytes per K row
-  static constexpr int VRow = kKeys * 2 + 16;  // bytes per V row [d][64]
+  static constexpr int KRow = D * 2;           // bytes per K row
   static constexpr int KBytes = kKeys * KRow;  // one K buffer
-  static constexpr int VBytes = D * VRow;      // one V buffer
-  static constexpr int V0 = 2 * KBytes;        // V buffers follow both K
+  static constexpr int VTile = kBlock * D * 2;  // one block's V tile
+  static constexpr int VBytes = 4 * VTile;      // one V buffer
+  static constexpr int V0 = 2 * KBytes;         // V buffers follow both K
   static constexpr int Total = 2 * KBytes + 2 * VBytes;
 };
+
+// Chunk swizzle of K row r (16 chunks of 16 bytes per row at D = 128, 8 at
+// D = 64).
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at lds + 16 l (lds uniform across the wave).
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+#endif
+}
+
+// Waits for every outstanding memory operation of the wave.
+__device__ __forceinline__ void wait_all_memory() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -290,7 +321,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   }
   const int tid = threadIdx.x;
   __builtin_assume(tid < kPfThreads);
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n32 = lane & 31;
   const int h = lane >> 5;
@@ -395,23 +426,30 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     return trow[blk < nblk ? blk : (nblk > 0 ? nblk - 1 : 0)];
   };
 
-  // Each block's 16 x D K tile (and V tile) is TPB = 2D chunks of 16 bytes;
-  // thread tid copies chunk tid % TPB of blocks bsub, bsub + NBV, ... of a
-  // step (bsub = tid / TPB, the same for a whole wave).
-  constexpr int TPB = 2 * D;
-  constexpr int NBV = kPfThreads / TPB;  // blocks copied side by side
-  constexpr int VPT = 4 / NBV;           // blocks per thread and step
-  static_assert(TPB % kWave == 0 && 4 % NBV == 0, "copy geometry");
-  const int bsub = __builtin_amdgcn_readfirstlane(tid / TPB);
-  const int within = tid % TPB;
-  const uint32_t within16 = (uint32_t)within * 16u;
+  // Copies go straight from the pool into LDS (global_load_lds_dwordx4:
+  // lane l of a wave instruction fills bytes 16 l .. 16 l + 15 of a 1 KiB
+  // LDS span, from any global address it names).  Wave w copies block w of
+  // each step: its K tile as IPT instructions of RPI rows each, and its V
+  // tile as IPT instructions of 32 d rows each.
+  constexpr int CPR = D / 8;             // 16-byte chunks per K row
+  constexpr int RPI = kWave / CPR;       // K rows per instruction
+  constexpr int IPT = kBlock / RPI;      // instructions per tile
+  static_assert(kPfWaves == 4 && IPT * 1024 == kBlock * D * 2, "copy geometry");
   const size_t tile_bytes = (size_t)kBlock * D * 2;
   const char* kp = reinterpret_cast<const char*>(k_pool) + (size_t)g * tile_bytes;
   const char* vp = reinterpret_cast<const char*>(v_pool) + (size_t)g * tile_bytes;
   const size_t blk_stride = (size_t)sc.Hkv * tile_bytes;
-  // LDS byte offsets of this thread's chunk within block 0 of a buffer
-  const int k_st = k_lds_row(within / (D / 8)) * Lay::KRow + (within % (D / 8)) * 16;
-  const int v_st = Lay::V0 + (within >> 1) * Lay::VRow + (within & 1) * 16;
+  // per lane: the tile offsets of its chunks in instruction m
+  uint32_t k_src[IPT], v_src[IPT];
+#pragma unroll
+  for (int m = 0; m < IPT; ++m) {
+    const int kr = kBlock * wave + RPI * m + lane / CPR;  // LDS row
+    const int key = k_lds_row(kr) & (kBlock - 1);         // token in block
+    k_src[m] = (uint32_t)(key * Lay::KRow +
+                          ((lane % CPR) ^ kswz<D>(kr)) * 16);
+    const int d = 32 * m + (lane >> 1);
+    v_src[m] = (uint32_t)(d * 32 + (((lane & 1) ^ ((d >> 3) & 1)) * 16));
+  }
 
   // Valid tokens of the 4 blocks of step s (0 past the end or for a bad
   // id), from the step's table entries (lane u % 4 holds block 4 s + u % 4).
@@ -425,47 +463,46 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
       nvo[u] = ok ? (v > kBlock ? kBlock : v) : 0;
     }
   };
-  auto load_tiles = [&](const char* pool, int ids_raw, u32x4 r[VPT]) {
+  // Issues the copies of a step (table entries ids_raw) into buffer buf.
+  auto issue_copies = [&](int buf, int ids_raw) {
+    const int raw = readlane(ids_raw, wave);
+    const int id = (unsigned)raw < (unsigned)sc.NB ? raw : 0;
+    const char* kb = kp + (size_t)id * blk_stride;  // uniform
+    const char* vb = vp + (size_t)id * blk_stride;
+    uint8_t* kl = lds + buf * Lay::KBytes + kBlock * wave * Lay::KRow;
+    uint8_t* vl = lds + Lay::V0 + buf * Lay::VBytes + wave * Lay::VTile;
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      const int raw = readlane(ids_raw, v * NBV + bsub);
-      const int id = (unsigned)raw < (unsigned)sc.NB ? raw : 0;
-      const char* blk_base = pool + (size_t)id * blk_stride;  // uniform
-      r[v] = *reinterpret_cast<const u32x4*>(blk_base + (uint32_t)within16);
+    for (int m = 0; m < IPT; ++m) {
+      copy16_to_lds(kb + k_src[m], kl + 1024 * m);
+      copy16_to_lds(vb + v_src[m], vl + 1024 * m);
     }
   };
-  auto store_k = [&](int kbuf, const u32x4 r[VPT]) {
-    uint8_t* base = lds + kbuf * Lay::KBytes + k_st;
+  // Zeroes V of tokens at or past nvs[u] in the V tiles of buffer buf (a
+  // masked probability times them must be 0, also where the slot holds NaN).
+  auto zero_v_tail = [&](int buf, const int nvs[4]) {
+    constexpr int CH = kBlock * D * 2 / 16;  // 16-byte chunks per V tile
 #pragma unroll
-    for (int v = 0; v < VPT; ++v)
-      *reinterpret_cast<u32x4*>(base + (v * NBV + bsub) * kBlock * Lay::KRow) =
-          r[v];
-  };
-  auto store_v = [&](int vbuf, const u32x4 r[VPT], const int nvs[4]) {
-    uint8_t* base = lds + vbuf * Lay::VBytes + v_st;
-    const bool all_full = nvs[0] == kBlock && nvs[1] == kBlock &&
-                          nvs[2] == kBlock && nvs[3] == kBlock;
-    if (all_full) {
-#pragma unroll
-      for (int v = 0; v < VPT; ++v)
-        *reinterpret_cast<u32x4*>(base + (v * NBV + bsub) * kBlock * 2) = r[v];
-    } else {
-      // zero V past the valid tokens of each block
-#pragma unroll
-      for (int v = 0; v < VPT; ++v) {
-        const int u = v * NBV + bsub;
-        const int nvb =
-            u == 0 ? nvs[0] : u == 1 ? nvs[1] : u == 2 ? nvs[2] : nvs[3];
-        *reinterpret_cast<u32x4*>(base + u * kBlock * 2) =
-            keep_below(r[v], nvb - 8 * (within & 1));
+    for (int u = 0; u < 4; ++u) {
+      if (nvs[u] >= kBlock) continue;
+      for (int c = tid; c < CH; c += kPfThreads) {
+        const int d = c >> 1;
+        const int half = (c & 1) ^ ((d >> 3) & 1);  // tokens 8 half .. + 7
+        u32x4* p = reinterpret_cast<u32x4*>(lds + Lay::V0 + buf * Lay::VBytes +
+                                            u * Lay::VTile + 16 * c);
+        *p = keep_below(*p, nvs[u] - 8 * half);
       }
     }
+  };
+  auto partial = [](const int nvs[4]) {
+    return nvs[0] < kBlock || nvs[1] < kBlock || nvs[2] < kBlock ||
+           nvs[3] < kBlock;
   };
 
   // lane-constant LDS offsets of the operands: K row n32 of each 32-key
   // half, d = 8h + 16c; V row d = n32 of each 32-row tile, keys 8h + 16c
-  const int k_off = n32 * Lay::KRow + 16 * h;
-  const int v_off = Lay::V0 + n32 * Lay::VRow + 16 * h;
+  const int k_off = n32 * Lay::KRow;
+  const int k_sw = kswz<D>(n32);  // the same for row 32 + n32
+  const int v_off = Lay::V0 + n32 * 32 + 16 * (h ^ ((n32 >> 3) & 1));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   // The two halves' products alternate (independent accumulators back to
   // back), and the K fragments are read kAhead products ahead.
@@ -477,8 +514,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[hf][i] = 0.f;
     auto frag = [&](int t) {  // product t: d chunk t / 2, half t % 2
+      const int chunk = (2 * (t >> 1) + h) ^ k_sw;
       return *reinterpret_cast<const bf16x8*>(base + (t & 1) * 32 * Lay::KRow +
-                                              32 * (t >> 1));
+                                              16 * chunk);
     };
     bf16x8 ring[kAhead];
 #pragma unroll
@@ -491,34 +529,31 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     }
   };
 
-  // Double-buffered steps: while the waves compute on step s (buffer
-  // s & 1), the step's loads of K and V of step s + 1 are in flight; they
-  // go to the other buffer at the end of the step.  Loads are issued
-  // unconditionally (past the end they repeat the last step, into a buffer
-  // nobody reads): loads under a branch would make the compiler wait for
-  // all of them before the first product.
   int nv_cur[4] = {0, 0, 0, 0};
-  int ids_next = 0;  // table entries of the next load
+  int ids_next = 0;  // table entries of the next copy
   const int last = s_end - 1;
   if (s_end > s_begin) {
     const int e0 = table_entry(s_begin);
-    u32x4 rk[VPT], rv[VPT];
-    load_tiles(kp, e0, rk);
-    load_tiles(vp, e0, rv);
+    issue_copies(0, e0);
     valid_of(s_begin, e0, nv_cur);
     ids_next = table_entry(last < s_begin + 1 ? last : s_begin + 1);
-    store_k(0, rk);
-    store_v(0, rv, nv_cur);
+    wait_all_memory();
+    __syncthreads();
+    if (partial(nv_cur)) {
+      zero_v_tail(0, nv_cur);
+      __syncthreads();
+    }
   }
-  __syncthreads();
 
+  // Double-buffered steps: while the waves compute on step s (buffer
+  // s & 1), the copies of step s + 1 into the other buffer are in flight;
+  // each step ends by waiting for them and a barrier (and, when a block of
+  // the next step is partly valid, zeroing its V tail behind one more).
   for (int s = s_begin; s < s_end; ++s) {
     const bool more = s < last;
     const int buf = (s - s_begin) & 1;
-    u32x4 rk[VPT], rv[VPT];
     int nv_next[4];
-    load_tiles(kp, ids_next, rk);  // step min(s + 1, last)
-    load_tiles(vp, ids_next, rv);
+    if (more) issue_copies(buf ^ 1, ids_next);
     valid_of(more ? s + 1 : s, ids_next, nv_next);
     ids_next = table_entry(s + 2 < last ? s + 2 : last);
 
@@ -583,8 +618,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     const uint8_t* vbase = lds + buf * Lay::VBytes + v_off;
     auto vfrag = [&](int t) {  // product t: chunk t / NX, d tile t % NX
       const int ch = t / NX, X = t % NX;
-      return *reinterpret_cast<const bf16x8*>(vbase + X * 32 * Lay::VRow +
-                                              ch * 32);
+      return *reinterpret_cast<const bf16x8*>(vbase + ch * Lay::VTile +
+                                              X * 32 * 32);
     };
     bf16x8 vring[kAhead];
 #pragma unroll
@@ -596,9 +631,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
       const int ch = t / NX;
       acc[t % NX] = mfma32(va, pb[ch >> 1][ch & 1], acc[t % NX]);
     }
-    store_k(buf ^ 1, rk);
-    store_v(buf ^ 1, rv, nv_next);
+    wait_all_memory();
     __syncthreads();
+    if (more && partial(nv_next)) {
+      zero_v_tail(buf ^ 1, nv_next);
+      __syncthreads();
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) nv_cur[u] = nv_next[u];
   }
