@@ -1,12 +1,18 @@
 // KV append: each new token's K row goes to its slot's row of the K tile
 // ([16][D] per block and KV head) and its V values to the slot's column of
-// the V tile ([D][16]).  A pure byte copy.
+// the V tile ([D][16]); a byte copy, or, for the quantising append, bf16
+// values divided by their tensor's scale and stored as fp8 e4m3fn codes.
 //
-// One thread per 16-byte chunk of a token's K row and one per 16-byte chunk
-// of its V row; token i owns workgroups [i * wpt, (i + 1) * wpt).  The chunk
-// loads do not depend on the slot, so a thread issues them together with the
-// slot load and pays one memory round trip before its stores: a K chunk is one 16-byte store, a V chunk
-// becomes 16 / sizeof(T) element stores one V-tile row (16 elements) apart.
+// One workgroup per (group of kGroup = 16 consecutive tokens, KV head).  A
+// thread item is one 16-byte chunk of a token's input row for that head:
+// its values go to one row of the K tile (a contiguous store) or to VPI rows
+// of the V tile, one element each.  K items are laid out chunk-fastest, so a
+// wave writes whole K rows; V items token-fastest, so 16 neighbouring lanes
+// hold the 16 tokens of the group at the same d: when those tokens fill
+// consecutive slots of one block (a prefill chunk), each V store instruction
+// writes contiguous 16-element row segments instead of isolated elements.
+// Every thread issues all of its chunk loads together with the slot loads,
+// so one memory round trip precedes its stores.
 #include "pa_launch.h"
 
 namespace pa {
@@ -14,38 +20,7 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T>
-__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
-    const T* __restrict__ k_new, const T* __restrict__ v_new,
-    const int32_t* __restrict__ slots, T* __restrict__ k_pool,
-    T* __restrict__ v_pool, int hkv, int d, int num_blocks, int wpt) {
-  constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  const int i = blockIdx.x / wpt;
-  const int chunks = hkv * d / E;  // chunks of one token's K (or V) row
-  int c = (blockIdx.x - i * wpt) * kAppendThreads + threadIdx.x;
-  const bool is_v = c >= chunks;
-  if (is_v) c -= chunks;
-  if (c >= chunks) return;
-  const size_t row = (size_t)i * hkv * d + (size_t)c * E;
-  const u32x4 val =
-      *reinterpret_cast<const u32x4*>((is_v ? v_new : k_new) + row);
-  const int slot = slots[i];
-  if (slot < 0 || slot >= num_blocks * kBlock) return;
-  const int phys = slot >> 4;
-  const int off = slot & (kBlock - 1);
-  const int g = c * E / d;
-  const int e0 = c * E - g * d;
-  const size_t tile = ((size_t)phys * hkv + g) * kBlock * d;
-  if (!is_v) {
-    *reinterpret_cast<u32x4*>(k_pool + tile + (size_t)off * d + e0) = val;
-  } else {
-    T el[E];
-    __builtin_memcpy(el, &val, sizeof(val));
-    T* vp = v_pool + tile + (size_t)e0 * kBlock + off;
-#pragma unroll
-    for (int e = 0; e < E; ++e) vp[e * kBlock] = el[e];
-  }
-}
+constexpr int kGroup = 16;  // tokens per workgroup
 
 // e4m3fn code of a float32 value: the nearest e4m3fn value, ties to the
 // even code, magnitudes above 448 saturated to 448, NaN to 0x7F.  Every step
@@ -68,69 +43,104 @@ __device__ __forceinline__ uint32_t e4m3fn_code(float v) {
   return code | sign;
 }
 
-// Quantising append: bf16 rows into an fp8 e4m3fn pool, each value divided
-// (IEEE float32 division) by its tensor's scale.  One thread per 8 input
-// values (16 bytes in, 8 bytes out), as in kv_append_kernel.
-__global__ __launch_bounds__(kAppendThreads) void kv_append_quant_kernel(
-    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int32_t* __restrict__ slots, uint8_t* __restrict__ k_pool,
-    uint8_t* __restrict__ v_pool, int hkv, int d, int num_blocks, int wpt,
-    float k_scale, float v_scale) {
-  constexpr int E = 8;
-  const int i = blockIdx.x / wpt;
-  const int chunks = hkv * d / E;
-  int c = (blockIdx.x - i * wpt) * kAppendThreads + threadIdx.x;
-  const bool is_v = c >= chunks;
-  if (is_v) c -= chunks;
-  if (c >= chunks) return;
-  const size_t row = (size_t)i * hkv * d + (size_t)c * E;
-  const u32x4 val =
-      *reinterpret_cast<const u32x4*>((is_v ? v_new : k_new) + row);
-  const int slot = slots[i];
-  if (slot < 0 || slot >= num_blocks * kBlock) return;
-  const float scale = is_v ? v_scale : k_scale;
-  uint32_t q[E];
+// Stored values of one 16-byte input chunk: a copy (TI = TO) or the
+// e4m3fn codes of bf16 values divided by `scale` (IEEE float32 division).
+template <typename TI, typename TO>
+struct Chunk {
+  static constexpr int N = 16 / (int)sizeof(TI);
+  TO v[N];
+  __device__ __forceinline__ Chunk(const u32x4& raw, float scale) {
+    if constexpr (sizeof(TI) == sizeof(TO)) {
+      (void)scale;
+      __builtin_memcpy(v, &raw, sizeof(raw));
+    } else {
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    q[2 * w] = e4m3fn_code(__uint_as_float(val[w] << 16) / scale);
-    q[2 * w + 1] = e4m3fn_code(__uint_as_float(val[w] & 0xFFFF0000u) / scale);
+      for (int w = 0; w < 4; ++w) {
+        v[2 * w] = (TO)e4m3fn_code(__uint_as_float(raw[w] << 16) / scale);
+        v[2 * w + 1] =
+            (TO)e4m3fn_code(__uint_as_float(raw[w] & 0xFFFF0000u) / scale);
+      }
+    }
   }
-  const int phys = slot >> 4;
-  const int off = slot & (kBlock - 1);
-  const int g = c * E / d;
-  const int e0 = c * E - g * d;
-  const size_t tile = ((size_t)phys * hkv + g) * kBlock * d;
-  if (!is_v) {
-    uint2 packed;
-    packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-    packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-    *reinterpret_cast<uint2*>(k_pool + tile + (size_t)off * d + e0) = packed;
-  } else {
-    uint8_t* vp = v_pool + tile + (size_t)e0 * kBlock + off;
+};
+
+template <typename TI, typename TO, int D>
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
+    const TI* __restrict__ k_new, const TI* __restrict__ v_new,
+    const int32_t* __restrict__ slots, TO* __restrict__ k_pool,
+    TO* __restrict__ v_pool, int n, int hkv, int num_blocks, float k_scale,
+    float v_scale) {
+  constexpr int VPI = 16 / (int)sizeof(TI);  // values per input chunk
+  constexpr int CPR = D / VPI;               // chunks per row and head
+  constexpr int ITEMS = kGroup * CPR;        // K items (and V items)
+  constexpr int NI = (2 * ITEMS + kAppendThreads - 1) / kAppendThreads;
+  const int g = (int)(blockIdx.x % (unsigned)hkv);
+  const int t0 = (int)(blockIdx.x / (unsigned)hkv) * kGroup;
+
+  int tok[NI], col[NI], slot[NI];
+  bool is_v[NI], live[NI];
+  u32x4 raw[NI];
 #pragma unroll
-    for (int e = 0; e < E; ++e) vp[e * kBlock] = (uint8_t)q[e];
+  for (int r = 0; r < NI; ++r) {
+    const int it = (int)threadIdx.x + r * kAppendThreads;
+    is_v[r] = it >= ITEMS;
+    const int j = is_v[r] ? it - ITEMS : it;
+    const int tt = is_v[r] ? j % kGroup : j / CPR;
+    col[r] = is_v[r] ? j / kGroup : j % CPR;
+    tok[r] = t0 + tt;
+    live[r] = it < 2 * ITEMS && tok[r] < n;
+    const TI* src = is_v[r] ? v_new : k_new;
+    const size_t at = ((size_t)tok[r] * hkv + g) * D + (size_t)col[r] * VPI;
+    raw[r] = live[r] ? *reinterpret_cast<const u32x4*>(src + at) : u32x4{};
+    slot[r] = live[r] ? slots[tok[r]] : -1;
+  }
+#pragma unroll
+  for (int r = 0; r < NI; ++r) {
+    if (!live[r] || slot[r] < 0 || slot[r] >= num_blocks * kBlock) continue;
+    const Chunk<TI, TO> ch(raw[r], is_v[r] ? v_scale : k_scale);
+    const int off = slot[r] & (kBlock - 1);
+    const size_t tile = ((size_t)(slot[r] >> 4) * hkv + g) * kBlock * D;
+    const int e0 = col[r] * VPI;
+    if (!is_v[r]) {
+      TO* kp = k_pool + tile + (size_t)off * D + e0;
+      if constexpr (VPI * sizeof(TO) == 16)
+        *reinterpret_cast<u32x4*>(kp) = *reinterpret_cast<const u32x4*>(ch.v);
+      else
+        *reinterpret_cast<uint2*>(kp) = *reinterpret_cast<const uint2*>(ch.v);
+    } else {
+      TO* vp = v_pool + tile + (size_t)e0 * kBlock + off;
+#pragma unroll
+      for (int e = 0; e < VPI; ++e) vp[e * kBlock] = ch.v[e];
+    }
   }
 }
 
-template <typename T>
-void launch_t(const void* k_new, const void* v_new, const int32_t* slots,
-              void* k_pool, void* v_pool, int n, int hkv, int d, int nb,
-              hipStream_t stream) {
-  const int wpt = append_workgroups_per_token((int)sizeof(T), hkv, d);
-  hipLaunchKernelGGL(kv_append_kernel<T>, dim3((unsigned)(n * wpt)),
-                     dim3(kAppendThreads), 0, stream,
-                     reinterpret_cast<const T*>(k_new),
-                     reinterpret_cast<const T*>(v_new), slots,
-                     reinterpret_cast<T*>(k_pool),
-                     reinterpret_cast<T*>(v_pool), hkv, d, nb, wpt);
+template <typename TI, typename TO>
+hipError_t launch_t(const void* k_new, const void* v_new, const int32_t* slots,
+                    void* k_pool, void* v_pool, int n, int hkv, int d, int nb,
+                    float k_scale, float v_scale, hipStream_t stream) {
+  const dim3 grid((unsigned)append_workgroups(n, hkv));
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kAppendThreads), 0, stream,
+                       reinterpret_cast<const TI*>(k_new),
+                       reinterpret_cast<const TI*>(v_new), slots,
+                       reinterpret_cast<TO*>(k_pool),
+                       reinterpret_cast<TO*>(v_pool), n, hkv, nb, k_scale,
+                       v_scale);
+  };
+  switch (d) {
+    case 64: go(kv_append_kernel<TI, TO, 64>); break;
+    case 128: go(kv_append_kernel<TI, TO, 128>); break;
+    case 256: go(kv_append_kernel<TI, TO, 256>); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
-int append_workgroups_per_token(int elem_bytes, int num_kv_heads,
-                                int head_size) {
-  const int chunks = num_kv_heads * head_size * elem_bytes / 16;
-  return (2 * chunks + kAppendThreads - 1) / kAppendThreads;
+int64_t append_workgroups(int64_t num_tokens, int num_kv_heads) {
+  return (num_tokens + kGroup - 1) / kGroup * num_kv_heads;
 }
 
 hipError_t launch_kv_append_quant(const void* k_new, const void* v_new,
@@ -140,15 +150,9 @@ hipError_t launch_kv_append_quant(const void* k_new, const void* v_new,
                                   int num_blocks, float k_scale,
                                   float v_scale, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  const int wpt = append_workgroups_per_token(2, num_kv_heads, head_size);
-  hipLaunchKernelGGL(kv_append_quant_kernel, dim3((unsigned)(num_tokens * wpt)),
-                     dim3(kAppendThreads), 0, stream,
-                     reinterpret_cast<const uint16_t*>(k_new),
-                     reinterpret_cast<const uint16_t*>(v_new), slots,
-                     reinterpret_cast<uint8_t*>(k_pool),
-                     reinterpret_cast<uint8_t*>(v_pool), num_kv_heads,
-                     head_size, num_blocks, wpt, k_scale, v_scale);
-  return hipGetLastError();
+  return launch_t<uint16_t, uint8_t>(k_new, v_new, slots, k_pool, v_pool,
+                                     num_tokens, num_kv_heads, head_size,
+                                     num_blocks, k_scale, v_scale, stream);
 }
 
 hipError_t launch_kv_append(int elem_bytes, const void* k_new,
@@ -159,21 +163,19 @@ hipError_t launch_kv_append(int elem_bytes, const void* k_new,
   if (num_tokens == 0) return hipSuccess;
   switch (elem_bytes) {
     case 1:
-      launch_t<uint8_t>(k_new, v_new, slots, k_pool, v_pool, num_tokens,
-                        num_kv_heads, head_size, num_blocks, stream);
-      break;
+      return launch_t<uint8_t, uint8_t>(k_new, v_new, slots, k_pool, v_pool,
+                                        num_tokens, num_kv_heads, head_size,
+                                        num_blocks, 1.f, 1.f, stream);
     case 2:
-      launch_t<uint16_t>(k_new, v_new, slots, k_pool, v_pool, num_tokens,
-                         num_kv_heads, head_size, num_blocks, stream);
-      break;
+      return launch_t<uint16_t, uint16_t>(k_new, v_new, slots, k_pool, v_pool,
+                                          num_tokens, num_kv_heads, head_size,
+                                          num_blocks, 1.f, 1.f, stream);
     case 4:
-      launch_t<uint32_t>(k_new, v_new, slots, k_pool, v_pool, num_tokens,
-                         num_kv_heads, head_size, num_blocks, stream);
-      break;
-    default:
-      return hipErrorInvalidValue;
+      return launch_t<uint32_t, uint32_t>(k_new, v_new, slots, k_pool, v_pool,
+                                          num_tokens, num_kv_heads, head_size,
+                                          num_blocks, 1.f, 1.f, stream);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -427,9 +427,7 @@ int pa_kv_append(const void* k_new, const void* v_new,
   const size_t eb = dtype_bytes(desc->kv_dtype);
   if (eb == 0) return PA_ERR_DTYPE;
   if ((int64_t)desc->num_kv_heads * desc->head_size > INT32_MAX / 16 ||
-      (int64_t)desc->num_tokens *
-              pa::append_workgroups_per_token((int)eb, desc->num_kv_heads,
-                                              desc->head_size) >
+      pa::append_workgroups(desc->num_tokens, desc->num_kv_heads) >
           INT32_MAX)
     return PA_ERR_SHAPE;
   if (desc->num_tokens == 0) return PA_OK;
@@ -460,9 +458,7 @@ int pa_kv_append_quant(const void* k_new, const void* v_new,
         isfinite(v_scale)))
     return PA_ERR_SHAPE;
   if ((int64_t)desc->num_kv_heads * desc->head_size > INT32_MAX / 16 ||
-      (int64_t)desc->num_tokens *
-              pa::append_workgroups_per_token(2, desc->num_kv_heads,
-                                              desc->head_size) >
+      pa::append_workgroups(desc->num_tokens, desc->num_kv_heads) >
           INT32_MAX)
     return PA_ERR_SHAPE;
   if (desc->num_tokens == 0) return PA_OK;

@@ -64,11 +64,10 @@ hipError_t launch_decode_merge_append(int kv_bytes, int head_size,
                                       const DecodeArgs& a,
                                       hipStream_t stream);
 
-// Byte copy of new tokens' K/V rows into pool slots: num_tokens *
-// append_workgroups_per_token(...) workgroups of kAppendThreads threads.
+// Byte copy of new tokens' K/V rows into pool slots: append_workgroups(...)
+// workgroups of kAppendThreads threads (one per 16 tokens and KV head).
 constexpr int kAppendThreads = 256;
-int append_workgroups_per_token(int elem_bytes, int num_kv_heads,
-                                int head_size);
+int64_t append_workgroups(int64_t num_tokens, int num_kv_heads);
 hipError_t launch_kv_append(int elem_bytes, const void* k_new,
                             const void* v_new, const int32_t* slots,
                             void* k_pool, void* v_pool, int num_tokens,
@@ -77,7 +76,7 @@ hipError_t launch_kv_append(int elem_bytes, const void* k_new,
 
 // Quantising append: bf16 rows into an fp8 e4m3fn pool (value / scale,
 // nearest e4m3fn code, ties to even, saturating at 448).  Same grid as
-// launch_kv_append with 2-byte input elements.
+// launch_kv_append.
 hipError_t launch_kv_append_quant(const void* k_new, const void* v_new,
                                   const int32_t* slots, void* k_pool,
                                   void* v_pool, int num_tokens,

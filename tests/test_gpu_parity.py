@@ -126,6 +126,75 @@ def test_kv_append_skips_negative_and_out_of_range_slots(gpu_lib):
                           v1.view(np.uint8).ravel())
 
 
+def _run_slots(nb, n_seqs, gen, max_len=70):
+    """Prefill-shaped slots: each sequence writes a run of consecutive
+    slots from a random offset of its first block through distinct random
+    blocks; two slots are then made invalid."""
+    blocks = torch.randperm(nb, generator=gen).tolist()
+    out = []
+    for _ in range(n_seqs):
+        off = int(torch.randint(0, 16, (1,), generator=gen))
+        length = int(torch.randint(1, max_len + 1, (1,), generator=gen))
+        nblk = (off + length + 15) // 16
+        mine, blocks = blocks[:nblk], blocks[nblk:]
+        out += [mine[(off + j) // 16] * 16 + (off + j) % 16
+                for j in range(length)]
+    slots = torch.tensor(out, dtype=torch.int32)
+    slots[len(out) // 3] = -1
+    slots[len(out) // 2] = nb * 16 + 5
+    return slots
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float8_e4m3fn,
+                                   torch.float32])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_kv_append_slot_runs_bit_exact(gpu_lib, dtype, d):
+    """Runs of consecutive slots (unaligned starts, token counts that are
+    not multiples of 16, invalid slots) land byte for byte where the oracle
+    puts them."""
+    from paged_kv_cache_451_amd import _lib
+    gen = torch.Generator().manual_seed(d)
+    hkv, nb = 4, 96
+    slots = _run_slots(nb, 7, gen)
+    n = len(slots)
+    size = 4 if dtype == torch.float32 else (1 if dtype == torch.float8_e4m3fn
+                                              else 2)
+    itype = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[size]
+
+    def rand_bits(shape):
+        b = torch.randint(0, 256, (*shape[:-1], shape[-1] * size),
+                          generator=gen, dtype=torch.uint8)
+        return b.view(itype).view(dtype)
+
+    k_pool = rand_bits((nb, hkv, 16, d))
+    v_pool = rand_bits((nb, hkv, d, 16))
+    k_new = rand_bits((n, hkv, d))
+    v_new = rand_bits((n, hkv, d))
+    kp, vp = k_pool.cuda(), v_pool.cuda()
+    _lib.pa_kv_append(k_new.cuda(), v_new.cuda(), slots.cuda(), kp, vp)
+    torch.cuda.synchronize()
+    k0 = raw(k_pool)[0]
+    v0 = raw(v_pool)[0]
+    k1, v1 = oracle.kv_append(k0, v0, raw(k_new)[0], raw(v_new)[0],
+                              slots.numpy())
+    assert np.array_equal(raw_bits(kp).ravel(), k1.view(np.uint8).ravel())
+    assert np.array_equal(raw_bits(vp).ravel(), v1.view(np.uint8).ravel())
+
+
+def test_quantising_append_slot_runs(gpu_lib):
+    gen = torch.Generator().manual_seed(29)
+    hkv, d, nb = 8, 128, 96
+    slots = _run_slots(nb, 9, gen)
+    n = len(slots)
+    k_new = torch.randn((n, hkv, d), generator=gen).to(torch.bfloat16)
+    v_new = (torch.randn((n, hkv, d), generator=gen) * 5).to(torch.bfloat16)
+    k_pool = torch.randint(0, 256, (nb, hkv, 16, d), generator=gen,
+                           dtype=torch.uint8).view(torch.float8_e4m3fn)
+    v_pool = torch.randint(0, 256, (nb, hkv, d, 16), generator=gen,
+                           dtype=torch.uint8).view(torch.float8_e4m3fn)
+    _quant_append_check(k_new, v_new, slots, k_pool, v_pool, 0.02, 0.03)
+
+
 # ---------------------------------------------------------------------------
 # decode: reduced sizes, every element, several split schedules
 # ---------------------------------------------------------------------------
