@@ -22,25 +22,17 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = 16;  // tokens per workgroup
 
-// e4m3fn code of a float32 value: the nearest e4m3fn value, ties to the
-// even code, magnitudes above 448 saturated to 448, NaN to 0x7F.  Every step
-// is exact (power-of-two scalings) except the final round-to-nearest-even
-// of rintf, so the code is fully determined by the float32 input.
-__device__ __forceinline__ uint32_t e4m3fn_code(float v) {
-  if (v != v) return 0x7Fu;
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  const float a = fminf(fabsf(v), 448.f);
-  uint32_t code;
-  if (a < 0.015625f) {
-    // subnormal range, steps of 2^-9; a result of 8 is the smallest normal
-    code = (uint32_t)rintf(a * 512.f);
-  } else {
-    const int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;
-    const float mant = ldexpf(a, -e);  // in [1, 2)
-    // a mantissa that rounds up to 8 carries into the exponent field
-    code = ((uint32_t)(e + 7) << 3) + (uint32_t)rintf((mant - 1.f) * 8.f);
-  }
-  return code | sign;
+// e4m3fn codes of two float32 values (low byte: a): the nearest e4m3fn
+// value, ties to the even code, magnitudes above 448 saturated to 448, NaN
+// to 0x7F.  The magnitude is clamped to 448 first, so the hardware
+// conversion (round to nearest even) never overflows.
+__device__ __forceinline__ uint32_t e4m3fn_pair(float a, float b) {
+  const float ca = fminf(fmaxf(a, -448.f), 448.f);
+  const float cb = fminf(fmaxf(b, -448.f), 448.f);
+  uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+  if (a != a) c = (c & 0xFF00u) | 0x7Fu;
+  if (b != b) c = (c & 0x00FFu) | 0x7F00u;
+  return c & 0xFFFFu;
 }
 
 // Stored values of one 16-byte input chunk: a copy (TI = TO) or the
@@ -56,9 +48,11 @@ struct Chunk {
     } else {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        v[2 * w] = (TO)e4m3fn_code(__uint_as_float(raw[w] << 16) / scale);
-        v[2 * w + 1] =
-            (TO)e4m3fn_code(__uint_as_float(raw[w] & 0xFFFF0000u) / scale);
+        const uint32_t c = e4m3fn_pair(__uint_as_float(raw[w] << 16) / scale,
+                                       __uint_as_float(raw[w] & 0xFFFF0000u) /
+                                           scale);
+        v[2 * w] = (TO)(c & 0xFFu);
+        v[2 * w + 1] = (TO)(c >> 8);
       }
     }
   }
