@@ -446,3 +446,37 @@ def build_prefill_case(cfg: PrefillConfig, seed: int = 0,
         block_tables=torch.from_numpy(tables),
         seq_lens=torch.from_numpy(seq_lens.astype(np.int32)),
         scale=float(np.float32(1.0 / math.sqrt(d))))
+
+
+# --------------------------------------------------------------------------
+# bulk appends and block copies (the append / copy-on-write benchmarks)
+# --------------------------------------------------------------------------
+def append_pool_blocks(tokens: int) -> int:
+    """Pool size for a bulk append: the blocks the tokens fill, plus 10%."""
+    need = -(-tokens // 16)
+    return need + need // 10 + 1
+
+
+def append_slots(tokens: int, num_blocks: int, pattern: str,
+                 seed: int = 0) -> torch.Tensor:
+    """Slots of a bulk append.  "runs": whole blocks of a shuffled pool
+    filled in order, as a prefill chunk lands; "scattered": a seeded random
+    set of distinct slots, as single-token decode appends land."""
+    rng = np.random.default_rng(seed)
+    if pattern == "runs":
+        t = np.arange(tokens)
+        s = rng.permutation(num_blocks)[t // 16] * 16 + t % 16
+    elif pattern == "scattered":
+        s = rng.permutation(num_blocks * 16)[:tokens]
+    else:
+        raise ValueError(pattern)
+    return torch.from_numpy(s.astype(np.int32))
+
+
+def copy_pairs(pairs: int, seed: int = 0):
+    """Pool size and distinct (source, destination) block lists of a
+    copy-on-write batch."""
+    nb = 2 * pairs + 16
+    perm = np.random.default_rng(seed).permutation(nb)
+    return (nb, torch.from_numpy(perm[:pairs].astype(np.int32)),
+            torch.from_numpy(perm[pairs:2 * pairs].astype(np.int32)))
