@@ -506,8 +506,48 @@ def bench_engine(a, torch):
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None,
                      "algorithmic_bytes_per_launch": int(np.mean(dec_bytes))},
-        "cpu_baseline": None,
+        "cpu_baseline": (None if a.no_cpu_baseline
+                         else engine_cpu_baseline(e, torch, a.cpu_seconds)),
     }), flush=True)
+
+
+def engine_cpu_baseline(e, torch, budget_s: float):
+    """The float64 decode oracle on the engine's running batch as the loop
+    left it (its pools, tables and lengths, random queries): whole
+    sequences in order until ~budget_s of CPU time; decoded tokens/s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from oracle.adapters import raw
+
+    ids = [r.req_id for r in e.running]
+    if not ids:
+        return None
+    tables, lens = e.mgr.tables(ids)
+    k, kv_dtype = raw(e.k_pool)
+    v, _ = raw(e.v_pool)
+    g = torch.Generator().manual_seed(7)
+    q, q_dtype = raw(torch.randn(len(ids), e.hq, e.d,
+                                 generator=g).to(torch.bfloat16))
+    done, t_total, tokens = 0, 0.0, 0
+    while t_total < budget_s and done < 64 * len(ids):
+        i = done % len(ids)
+        t0 = time.perf_counter()
+        oracle.paged_decode(q, k, v, tables, lens, e.scale, q_dtype=q_dtype,
+                            kv_dtype=kv_dtype, seqs=[i])
+        t_total += time.perf_counter() - t0
+        tokens += int(lens[i])
+        done += 1
+    threads = max((t.get("num_threads", 1) for t in threadpool_info()),
+                  default=1)
+    return {"value": round(done / t_total, 3), "unit": "tokens/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"float64 numpy oracle, {done} sequence decodes taken "
+                      f"in order from the {len(ids)} running requests at the "
+                      f"end of the loop ({tokens} context tokens, "
+                      f"{t_total:.1f} s); decoded tokens per second",
+            "context_tokens_per_s": round(tokens / t_total, 1)}
 
 
 def main():
