@@ -572,11 +572,18 @@ def _quant_append_check(k_new, v_new, slots, k_pool, v_pool, ks, vs):
     assert np.array_equal(raw_bits(vp).ravel(), v1.ravel())
 
 
-@pytest.mark.parametrize("ks, vs", [(1.0, 1.0), (0.0123, 1.0 / 448),
-                                    (3.7, 0.5)])
+_F32 = np.finfo(np.float32)
+
+
+@pytest.mark.parametrize("ks, vs", [
+    (1.0, 1.0), (0.0123, 1.0 / 448), (3.7, 0.5), (1.0 / 3, 0.1),
+    (float(_F32.smallest_subnormal), float(_F32.max)),
+    (float(_F32.tiny), float(np.nextafter(np.float32(2), np.float32(0))))])
 def test_quantising_append_every_bf16_code(gpu_lib, ks, vs):
     """All 65536 bf16 codes (NaN, infinities, subnormals, every e4m3fn tie
-    that bf16 can hold at scale 1) as K and, reversed, as V."""
+    that bf16 can hold at scale 1) as K and, reversed, as V, at ordinary
+    scales and at the float32 extremes (the kernel divides by multiplying
+    with a float64 reciprocal)."""
     hkv, d, n, nb = 8, 128, 64, 80
     codes = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16)
     k_new = codes.view(torch.bfloat16).reshape(n, hkv, d).contiguous()
