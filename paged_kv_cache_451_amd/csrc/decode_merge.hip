@@ -15,6 +15,37 @@
 namespace pa {
 namespace {
 
+// Value of lane l ^ 1, l ^ 2 (quad permutations), of the other quad of the
+// lane's 8 (row half-mirror) and of the other 8 of its 16 (row mirror):
+// DPP moves, without an LDS round trip.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                         0xF, 0xF, false));
+}
+
+// Sum or maximum over the 64 lanes, left in every lane.  After the two quad
+// steps every lane of a quad holds the quad's result; each mirror step then
+// pairs a group with the other half of its row, and the two swaps pair a
+// row with the rows 16 and 32 lanes away.
+template <bool kMax>
+__device__ __forceinline__ float wave_all(float v) {
+  auto op = [](float a, float b) { return kMax ? fmaxf(a, b) : a + b; };
+  v = op(v, dpp_move<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_move<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_move<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_move<0x140>(v));  // row_mirror
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = op(__builtin_bit_cast(float, (unsigned)r16[0]),
+         __builtin_bit_cast(float, (unsigned)r16[1]));
+  const unsigned w = __builtin_bit_cast(unsigned, v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return op(__builtin_bit_cast(float, (unsigned)r32[0]),
+            __builtin_bit_cast(float, (unsigned)r32[1]));
+}
+
 // Row of partial `k` (a range index) for sequence span starting at block
 // Sb, or -1 when range k is empty and left no partial.
 __device__ __forceinline__ int partial_row(int k, int Sb, int U, int g,
@@ -60,16 +91,12 @@ __device__ inline void fold_range_partials(
       }
     };
     load_rows(0);
-    float mx = mi;
-#pragma unroll
-    for (int x = 1; x < kWave; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x, kWave));
+    const float mx = wave_all<true>(mi);
     const float m_new = fmaxf(M, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(M - m_use);
     const float wi = row >= 0 ? fast_exp2(mi - m_use) : 0.f;
-    float wl = wi * li;
-#pragma unroll
-    for (int x = 1; x < kWave; x <<= 1) wl += __shfl_xor(wl, x, kWave);
+    const float wl = wave_all<false>(wi * li);
     lsum = lsum * alpha + wl;
 #pragma unroll
     for (int r = 0; r < NR; ++r) o[r] *= alpha;
@@ -167,7 +194,9 @@ struct KvElem<1> {
 // In cascade decode the main pass covered only each sequence's suffix
 // blocks; the shared-prefix pass's partial is folded in as one more term
 // (when it holds any weight), and `full_lens` gives the true lengths.
-template <int KB, int D>
+// kShared selects the cascade form at compile time, so that the plain step
+// holds no registers for the shared partials.
+template <int KB, int D, bool kShared>
 __global__ __launch_bounds__(64) void decode_merge_append_kernel(
     typename KvElem<KB>::io* __restrict__ out_all,
     const typename KvElem<KB>::io* __restrict__ q,
@@ -201,12 +230,13 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(
   const int L = full_lens ? full_lens[b] : seq_lens[b];
   const int slot = slots[b];
   // shared-prefix partials, one per key range (all issued up front)
-  float sh_m[kMaxSharedSplits], sh_l[kMaxSharedSplits];
-  float sh_o[kMaxSharedSplits][NR];
+  constexpr int NS = kShared ? kMaxSharedSplits : 1;
+  float sh_m[NS], sh_l[NS];
+  float sh_o[NS][NR];
   const size_t split_rows = (size_t)s.B * s.Hq;
 #pragma unroll
-  for (int k = 0; k < kMaxSharedSplits; ++k) {
-    const bool live = shared_ml && k < shared_splits;
+  for (int k = 0; k < NS; ++k) {
+    const bool live = kShared && k < shared_splits;
     const size_t r = (size_t)k * split_rows + h_row;
     sh_m[k] = live ? shared_ml[r * 2] : -INFINITY;
     sh_l[k] = live ? shared_ml[r * 2 + 1] : 0.f;
@@ -238,8 +268,7 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(
   float dot = 0.f;
 #pragma unroll
   for (int r = 0; r < NR; ++r) dot = fmaf(qf[r], E::value(kr[r]), dot);
-#pragma unroll
-  for (int x = 1; x < kWave; x <<= 1) dot += __shfl_xor(dot, x, kWave);
+  dot = wave_all<false>(dot);
 
   float M = -INFINITY, lsum = 0.f;
   float o[NR];
@@ -258,10 +287,10 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(
                              lsum, o);
     }
   }
-  if (shared_ml) {  // the shared prefix's partials, as more terms
+  if constexpr (kShared) {  // the shared prefix's partials, as more terms
     float m_new = M;
 #pragma unroll
-    for (int k = 0; k < kMaxSharedSplits; ++k)
+    for (int k = 0; k < NS; ++k)
       if (sh_l[k] > 0.f) m_new = fmaxf(m_new, sh_m[k]);
     if (m_new > -INFINITY) {
       const float alpha = fast_exp2(M - m_new);
@@ -269,7 +298,7 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(
 #pragma unroll
       for (int r = 0; r < NR; ++r) o[r] *= alpha;
 #pragma unroll
-      for (int k = 0; k < kMaxSharedSplits; ++k) {
+      for (int k = 0; k < NS; ++k) {
         // a range with no weight is skipped, not multiplied by zero: its
         // output row was never written
         if (!(sh_l[k] > 0.f)) continue;
@@ -317,12 +346,12 @@ hipError_t launch_m(int head_size, const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int KB, int D>
-void launch_append_one(const DecodeArgs& a, hipStream_t stream) {
+template <int KB, int D, bool kShared>
+void launch_append_k(const DecodeArgs& a, hipStream_t stream) {
   typedef KvElem<KB> E;
   const dim3 grid((unsigned)(a.s.B * a.s.Hq));
   hipLaunchKernelGGL(
-      (decode_merge_append_kernel<KB, D>), grid, dim3(64), 0, stream,
+      (decode_merge_append_kernel<KB, D, kShared>), grid, dim3(64), 0, stream,
       reinterpret_cast<typename E::io*>(a.out),
       reinterpret_cast<const typename E::io*>(a.q), a.prefix, a.seq_lens,
       a.slots, reinterpret_cast<const typename E::raw*>(a.k_new),
@@ -331,6 +360,14 @@ void launch_append_one(const DecodeArgs& a, hipStream_t stream) {
       reinterpret_cast<typename E::raw*>(a.v_pool_w), a.part_ml, a.part_o,
       a.direct_ml, a.direct_o, a.shared_ml, a.shared_o, a.shared_splits,
       a.full_lens, a.s);
+}
+
+template <int KB, int D>
+void launch_append_one(const DecodeArgs& a, hipStream_t stream) {
+  if (a.shared_ml)
+    launch_append_k<KB, D, true>(a, stream);
+  else
+    launch_append_k<KB, D, false>(a, stream);
 }
 
 template <int KB>
