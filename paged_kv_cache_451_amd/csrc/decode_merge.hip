@@ -327,6 +327,207 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(
   for (int r = 0; r < NR; ++r) out[lane + 64 * r] = (OT)(o[r] * inv);
 }
 
+// Sum or maximum over each half (32 lanes) of the wave, left in every lane
+// of that half: the quad and mirror steps of wave_all, then the swap with
+// the row 16 lanes away.
+template <bool kMax>
+__device__ __forceinline__ float half_all(float v) {
+  auto op = [](float a, float b) { return kMax ? fmaxf(a, b) : a + b; };
+  v = op(v, dpp_move<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_move<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_move<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_move<0x140>(v));  // row_mirror
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return op(__builtin_bit_cast(float, (unsigned)r16[0]),
+            __builtin_bit_cast(float, (unsigned)r16[1]));
+}
+
+// Value of lane `base + t` for lanes of the first half, `32 + base + t`
+// for the second (t uniform).
+__device__ __forceinline__ int half_lane(int v, int t, bool upper) {
+  const int lo = readlane(v, t);
+  const int hi = readlane(v, 32 + t);
+  return upper ? hi : lo;
+}
+
+// The range partials kf..kl of sequence span [Sb, ...) folded into the
+// running (M, lsum, o) of one query head per half wave (KV head g, head n
+// within its group).  Partials are consumed 32 at a time (half lane i holds
+// partial i0 + i's m and l); their output rows are read kRows at a time,
+// the first batch issued before the (m, l) reductions so that both loads
+// share one memory round trip.  Lane il of a half owns columns il + 32 r.
+template <int D>
+__device__ inline void fold_range_partials_half(
+    int kf, int kl, int Sb, int U, int g, int n, bool upper, const Sched& s,
+    const float* __restrict__ part_ml, const float* __restrict__ part_o,
+    float& M, float& lsum, float (&o)[D / 32]) {
+  constexpr int NR = D / 32;
+  constexpr int kRows = 8;
+  const int il = threadIdx.x & 31;
+  const int np = kl - kf + 1;
+  for (int i0 = 0; i0 < np; i0 += 32) {
+    const int cnt = np - i0 < 32 ? np - i0 : 32;
+    const int row = il < cnt ? partial_row(kf + i0 + il, Sb, U, g, n, s) : -1;
+    float mi = -INFINITY, li = 0.f;
+    if (row >= 0) {
+      mi = part_ml[(size_t)row * 2];
+      li = part_ml[(size_t)row * 2 + 1];
+    }
+    float v[kRows][NR];
+    auto load_rows = [&](int t0) {
+#pragma unroll
+      for (int u = 0; u < kRows; ++u) {
+        const int rr = t0 + u < cnt ? half_lane(row, t0 + u, upper) : -1;
+        const float* po = part_o + (size_t)(rr < 0 ? 0 : rr) * D + il;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) v[u][r] = rr < 0 ? 0.f : po[32 * r];
+      }
+    };
+    load_rows(0);
+    const float mx = half_all<true>(mi);
+    const float m_new = fmaxf(M, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(M - m_use);
+    const float wi = row >= 0 ? fast_exp2(mi - m_use) : 0.f;
+    const float wl = half_all<false>(wi * li);
+    lsum = lsum * alpha + wl;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) o[r] *= alpha;
+    M = m_new;
+    for (int t0 = 0; t0 < cnt; t0 += kRows) {
+      if (t0 > 0) load_rows(t0);
+#pragma unroll
+      for (int u = 0; u < kRows; ++u) {
+        const int tt = t0 + u < cnt ? t0 + u : 0;
+        const float w = __builtin_bit_cast(
+            float, half_lane(__builtin_bit_cast(int, wi), tt, upper));
+#pragma unroll
+        for (int r = 0; r < NR; ++r) o[r] = fmaf(w, v[u][r], o[r]);
+      }
+    }
+  }
+}
+
+// The same merge pass with one 64-lane workgroup per (sequence, pair of
+// query heads), for batches whose (sequence, query head) count exceeds the
+// waves the GPU holds at once: the first half of the wave takes head 2p,
+// the second head 2p + 1, so the sequence's lengths and ranges are read
+// once for both and half as many waves run.  (When the batch fits in one
+// round, one head per wave is faster: more loads in flight.)  The main
+// pass attended to every cached token but the newest one
+// (len_bias = 1) and left partials: range partials for sequences split
+// between ranges, a direct partial for a sequence one range finished.  For
+// its query head, each half
+//   * writes the newest token's K row and V column for KV head g into its
+//     slot (the half of the group's first query head; a byte copy),
+//   * scores that token from k_new (s = scale * log2e * k_scale * <q, k>),
+//   * and folds it into the sequence's partials as one more term of the
+//     online softmax:  out = (sum_i w_i o_i + 2^(s-M) v_scale v_new) /
+//                            (sum_i w_i l_i + 2^(s-M)).
+// The pool slot is not read by this call's main pass (its position is at or
+// past the attended length), so the write needs no ordering with it.
+// (The cascade form always uses one head per wave.)  With an odd number of
+// query heads the second half of the last workgroup of a sequence has no head:
+// it loads from a valid row and stores nothing.
+template <int KB, int D>
+__global__ __launch_bounds__(64) void decode_merge_append_pair_kernel(
+    typename KvElem<KB>::io* __restrict__ out_all,
+    const typename KvElem<KB>::io* __restrict__ q,
+    const int32_t* __restrict__ prefix, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ slots,
+    const typename KvElem<KB>::raw* __restrict__ k_new,
+    const typename KvElem<KB>::raw* __restrict__ v_new,
+    typename KvElem<KB>::raw* __restrict__ k_pool,
+    typename KvElem<KB>::raw* __restrict__ v_pool,
+    const float* __restrict__ part_ml, const float* __restrict__ part_o,
+    const float* __restrict__ direct_ml, const float* __restrict__ direct_o,
+    Sched s) {
+  typedef KvElem<KB> E;
+  typedef typename E::io OT;
+  typedef typename E::raw RT;
+  constexpr int NR = D / 32;
+  const int lane = threadIdx.x;
+  const bool upper = lane >= 32;
+  const int il = lane & 31;
+  const int G = s.G;
+  const int pairs = (s.Hq + 1) >> 1;
+  const int b = blockIdx.x / pairs;
+  const int h_raw = 2 * (blockIdx.x % pairs) + (upper ? 1 : 0);
+  const bool has_head = h_raw < s.Hq;
+  const int h = has_head ? h_raw : s.Hq - 1;  // a valid row to read
+  const int g = h / G;
+  const int n = h % G;
+  const size_t h_row = (size_t)b * s.Hq + h;
+  const size_t kv_row = ((size_t)b * s.Hkv + g) * D;
+
+  // independent loads: one memory round trip
+  const int Sb = prefix[b];
+  const int Sb1 = prefix[b + 1];
+  const int U = prefix[s.B];
+  const int L = seq_lens[b];
+  const int slot = slots[b];
+  RT kr[NR], vr[NR];
+  float qf[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int d = il + 32 * r;
+    kr[r] = k_new[kv_row + d];
+    vr[r] = v_new[kv_row + d];
+    qf[r] = (float)q[h_row * D + d];
+  }
+
+  if (has_head && n == 0 && slot >= 0 && slot < s.NB * kBlock) {
+    const size_t tile = ((size_t)(slot >> 4) * s.Hkv + g) * kBlock * D;
+    const int off = slot & (kBlock - 1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int d = il + 32 * r;
+      k_pool[tile + (size_t)off * D + d] = kr[r];
+      v_pool[tile + (size_t)d * kBlock + off] = vr[r];
+    }
+  }
+
+  float dot = 0.f;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) dot = fmaf(qf[r], E::value(kr[r]), dot);
+  dot = half_all<false>(dot);
+
+  float M = -INFINITY, lsum = 0.f;
+  float o[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) o[r] = 0.f;
+  if (Sb1 > Sb) {
+    const int kf = range_of(Sb, U, s.Wh);
+    const int kl = range_of(Sb1 - 1, U, s.Wh);
+    if (kf == kl) {
+      M = direct_ml[h_row * 2];
+      lsum = direct_ml[h_row * 2 + 1];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) o[r] = direct_o[h_row * D + il + 32 * r];
+    } else {
+      fold_range_partials_half<D>(kf, kl, Sb, U, g, n, upper, s, part_ml,
+                                  part_o, M, lsum, o);
+    }
+  }
+  if (L >= 1) {  // the newest token, from k_new / v_new
+    const float sn = dot * s.c_log2;
+    const float m_new = fmaxf(M, sn);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(M - m_use);
+    const float w = fast_exp2(sn - m_use);
+    lsum = lsum * alpha + w;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      o[r] = fmaf(w * s.v_scale, E::value(vr[r]), o[r] * alpha);
+  }
+  if (!has_head) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  OT* out = out_all + h_row * D;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) out[il + 32 * r] = (OT)(o[r] * inv);
+}
+
 template <typename OT, int D>
 void launch_one(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.s.B * a.s.Hq));
@@ -364,10 +565,23 @@ void launch_append_k(const DecodeArgs& a, hipStream_t stream) {
 
 template <int KB, int D>
 void launch_append_one(const DecodeArgs& a, hipStream_t stream) {
-  if (a.shared_ml)
+  if (a.shared_ml) {
     launch_append_k<KB, D, true>(a, stream);
-  else
+  } else if (a.merge_pairs) {
+    typedef KvElem<KB> E;
+    const dim3 grid((unsigned)(a.s.B * ((a.s.Hq + 1) / 2)));
+    hipLaunchKernelGGL(
+        (decode_merge_append_pair_kernel<KB, D>), grid, dim3(64), 0, stream,
+        reinterpret_cast<typename E::io*>(a.out),
+        reinterpret_cast<const typename E::io*>(a.q), a.prefix, a.seq_lens,
+        a.slots, reinterpret_cast<const typename E::raw*>(a.k_new),
+        reinterpret_cast<const typename E::raw*>(a.v_new),
+        reinterpret_cast<typename E::raw*>(a.k_pool_w),
+        reinterpret_cast<typename E::raw*>(a.v_pool_w), a.part_ml, a.part_o,
+        a.direct_ml, a.direct_o, a.s);
+  } else {
     launch_append_k<KB, D, false>(a, stream);
+  }
 }
 
 template <int KB>
@@ -394,6 +608,30 @@ hipError_t launch_decode_merge_append(int kv_bytes, int head_size,
     case 1: return launch_append_d<1>(head_size, a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+int occupancy_decode_merge_append(int kv_bytes, int head_size) {
+  const void* f = nullptr;
+#define PA_MERGE_KERNEL(KB, D) \
+  reinterpret_cast<const void*>(decode_merge_append_kernel<KB, D, false>)
+  switch (kv_bytes * 1000 + head_size) {
+    case 4064: f = PA_MERGE_KERNEL(4, 64); break;
+    case 4128: f = PA_MERGE_KERNEL(4, 128); break;
+    case 4256: f = PA_MERGE_KERNEL(4, 256); break;
+    case 2064: f = PA_MERGE_KERNEL(2, 64); break;
+    case 2128: f = PA_MERGE_KERNEL(2, 128); break;
+    case 2256: f = PA_MERGE_KERNEL(2, 256); break;
+    case 1064: f = PA_MERGE_KERNEL(1, 64); break;
+    case 1128: f = PA_MERGE_KERNEL(1, 128); break;
+    case 1256: f = PA_MERGE_KERNEL(1, 256); break;
+    default: return 0;
+  }
+#undef PA_MERGE_KERNEL
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64, 0) !=
+      hipSuccess)
+    return 0;
+  return n;
 }
 
 hipError_t launch_decode_merge(bool out_bf16, int head_size,

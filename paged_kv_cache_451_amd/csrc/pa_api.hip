@@ -256,6 +256,7 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
   a.shared_o = nullptr;
   a.shared_splits = 0;
   a.full_lens = nullptr;
+  a.merge_pairs = false;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(
@@ -315,9 +316,18 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
   if (e != hipSuccess) return PA_ERR_LAUNCH;
   if (!cascade && ev[1] && hipEventRecord(ev[1], s) != hipSuccess)
     return PA_ERR_LAUNCH;
-  if (fused)
-    e = pa::launch_decode_merge_append((int)dtype_bytes(desc->kv_dtype),
-                                       desc->head_size, a, s);
+  if (fused) {
+    // One query head per merge workgroup while the whole grid fits on the
+    // GPU at once (more loads in flight); two per workgroup beyond that, so
+    // a large batch still takes one round of waves.
+    const int kb = (int)dtype_bytes(desc->kv_dtype);
+    const int64_t resident =
+        (int64_t)pa::occupancy_decode_merge_append(kb, desc->head_size) *
+        cu_count();
+    a.merge_pairs = !a.shared_ml && resident > 0 &&
+                    (int64_t)desc->num_seqs * desc->num_q_heads > resident;
+    e = pa::launch_decode_merge_append(kb, desc->head_size, a, s);
+  }
   else
     e = pa::launch_decode_merge(desc->q_dtype == PA_BF16, desc->head_size, a,
                                 s);

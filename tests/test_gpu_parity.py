@@ -516,6 +516,32 @@ def test_fused_step_edge_shapes(gpu_lib, spec, waves):
     assert max_err(out, oracle_out(case)) <= TOL[case.config.kv_dtype]
 
 
+# Batches with more (sequence, query head) pairs than the GPU holds merge
+# workgroups at once (at most 32 per CU on 256 CUs = 8192) take the merge
+# pass with two query heads per workgroup.  These cases have at least 1.5x
+# that many pairs of short sequences, so that path runs; they cover an odd
+# head count, pairs whose halves belong to different KV heads, fp8, fp32
+# and every head size.
+MANY = [
+    dict(hq=5, hkv=5, d=64),                               # odd Hq, G = 1
+    dict(hq=6, hkv=2, d=128),                              # G = 3
+    dict(hq=8, hkv=2, d=256, kv_dtype="fp8_e4m3fn"),       # fp8, D = 256
+    dict(hq=2, hkv=2, d=64, q_dtype="f32", kv_dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("spec", MANY)
+def test_fused_step_many_short_sequences(gpu_lib, spec):
+    n = -(-12288 // spec["hq"])
+    lens = np.random.default_rng(11).integers(1, 49, n).tolist()
+    case = _custom_case(lens, seed=12, **spec)
+    out, dev = run_fused(case)
+    assert_pools_equal_oracle_append(case, dev)
+    err = max_err(out, oracle_out(case))
+    print(f"fused, {n} sequences x {spec['hq']} heads: max abs err {err:.3e}")
+    assert err <= TOL[case.config.kv_dtype]
+
+
 def test_fused_step_dominant_new_token(gpu_lib):
     """The newest token carries a large key along q: its weight is ~1 and
     the output is its V row, which only k_new / v_new hold before the call
