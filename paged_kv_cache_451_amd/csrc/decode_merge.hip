@@ -528,8 +528,65 @@ __global__ __launch_bounds__(64) void decode_merge_append_pair_kernel(
   for (int r = 0; r < NR; ++r) out[il + 32 * r] = (OT)(o[r] * inv);
 }
 
+// The plain merge pass with one 64-lane workgroup per (sequence, pair of
+// query heads), for batches with more (sequence, query head) pairs than the
+// GPU holds merge workgroups at once: the first half of the wave takes head
+// 2p, the second head 2p + 1.  With an odd number of query heads the second
+// half of a sequence's last workgroup has no head and stores nothing.
+template <typename OT, int D>
+__global__ __launch_bounds__(64) void decode_merge_pair_kernel(
+    OT* __restrict__ out_all, const int32_t* __restrict__ prefix,
+    const float* __restrict__ part_ml, const float* __restrict__ part_o,
+    Sched s) {
+  constexpr int NR = D / 32;
+  const int lane = threadIdx.x;
+  const bool upper = lane >= 32;
+  const int il = lane & 31;
+  const int G = s.G;
+  const int pairs = (s.Hq + 1) >> 1;
+  const int b = blockIdx.x / pairs;
+  const int h_raw = 2 * (blockIdx.x % pairs) + (upper ? 1 : 0);
+  const bool has_head = h_raw < s.Hq;
+  const int h = has_head ? h_raw : s.Hq - 1;
+  const int g = h / G;
+  const int n = h % G;
+  const int Sb = prefix[b];
+  const int Sb1 = prefix[b + 1];
+  const int U = prefix[s.B];
+  OT* out = out_all + ((size_t)b * s.Hq + h) * D;
+
+  if (Sb1 == Sb) {
+    if (has_head) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) out[il + 32 * r] = (OT)0.f;
+    }
+    return;
+  }
+  const int kf = range_of(Sb, U, s.Wh);
+  const int kl = range_of(Sb1 - 1, U, s.Wh);
+  if (kf == kl) return;  // finished by the main pass
+
+  float M = -INFINITY, lsum = 0.f;
+  float o[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) o[r] = 0.f;
+  fold_range_partials_half<D>(kf, kl, Sb, U, g, n, upper, s, part_ml, part_o,
+                              M, lsum, o);
+  if (!has_head) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) out[il + 32 * r] = (OT)(o[r] * inv);
+}
+
 template <typename OT, int D>
 void launch_one(const DecodeArgs& a, hipStream_t stream) {
+  if (a.merge_pairs) {
+    const dim3 grid((unsigned)(a.s.B * ((a.s.Hq + 1) / 2)));
+    hipLaunchKernelGGL((decode_merge_pair_kernel<OT, D>), grid, dim3(64), 0,
+                       stream, reinterpret_cast<OT*>(a.out), a.prefix,
+                       a.part_ml, a.part_o, a.s);
+    return;
+  }
   const dim3 grid((unsigned)(a.s.B * a.s.Hq));
   hipLaunchKernelGGL((decode_merge_kernel<OT, D>), grid, dim3(64), 0, stream,
                      reinterpret_cast<OT*>(a.out), a.prefix, a.part_ml,
@@ -627,6 +684,30 @@ int occupancy_decode_merge_append(int kv_bytes, int head_size) {
     default: return 0;
   }
 #undef PA_MERGE_KERNEL
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64, 0) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+
+int occupancy_decode_merge(bool out_bf16, int head_size) {
+  const void* f = nullptr;
+  switch (head_size) {
+    case 64:
+      f = out_bf16 ? reinterpret_cast<const void*>(decode_merge_kernel<__bf16, 64>)
+                   : reinterpret_cast<const void*>(decode_merge_kernel<float, 64>);
+      break;
+    case 128:
+      f = out_bf16 ? reinterpret_cast<const void*>(decode_merge_kernel<__bf16, 128>)
+                   : reinterpret_cast<const void*>(decode_merge_kernel<float, 128>);
+      break;
+    case 256:
+      f = out_bf16 ? reinterpret_cast<const void*>(decode_merge_kernel<__bf16, 256>)
+                   : reinterpret_cast<const void*>(decode_merge_kernel<float, 256>);
+      break;
+    default: return 0;
+  }
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64, 0) !=
       hipSuccess)

@@ -327,10 +327,15 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
     a.merge_pairs = !a.shared_ml && resident > 0 &&
                     (int64_t)desc->num_seqs * desc->num_q_heads > resident;
     e = pa::launch_decode_merge_append(kb, desc->head_size, a, s);
+  } else {
+    const bool bf16 = desc->q_dtype == PA_BF16;
+    const int64_t resident =
+        (int64_t)pa::occupancy_decode_merge(bf16, desc->head_size) *
+        cu_count();
+    a.merge_pairs = resident > 0 &&
+                    (int64_t)desc->num_seqs * desc->num_q_heads > resident;
+    e = pa::launch_decode_merge(bf16, desc->head_size, a, s);
   }
-  else
-    e = pa::launch_decode_merge(desc->q_dtype == PA_BF16, desc->head_size, a,
-                                s);
   if (e != hipSuccess) return PA_ERR_LAUNCH;
   if (cascade && ev[1] && hipEventRecord(ev[1], s) != hipSuccess)
     return PA_ERR_LAUNCH;

@@ -39,8 +39,8 @@ struct DecodeArgs {
   const float* shared_o;   // [shared_splits][B][Hq][D]
   int shared_splits;
   const int32_t* full_lens;
-  // Fused merge pass without a shared prefix: one workgroup per (sequence,
-  // pair of query heads) instead of per (sequence, query head).
+  // Merge pass (plain, or fused without a shared prefix): one workgroup per
+  // (sequence, pair of query heads) instead of per (sequence, query head).
   bool merge_pairs;
   Sched s;
 };
@@ -69,6 +69,8 @@ hipError_t launch_decode_merge_append(int kv_bytes, int head_size,
 // Resident workgroups per compute unit of the fused merge pass with one
 // query head per workgroup (0 on error).
 int occupancy_decode_merge_append(int kv_bytes, int head_size);
+// The same for the plain merge pass.
+int occupancy_decode_merge(bool out_bf16, int head_size);
 
 // Byte copy of new tokens' K/V rows into pool slots: append_workgroups(...)
 // workgroups of kAppendThreads threads (one per 16 tokens and KV head).

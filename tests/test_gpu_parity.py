@@ -518,7 +518,7 @@ def test_fused_step_edge_shapes(gpu_lib, spec, waves):
 
 # Batches with more (sequence, query head) pairs than the GPU holds merge
 # workgroups at once (at most 32 per CU on 256 CUs = 8192) take the merge
-# pass with two query heads per workgroup.  These cases have at least 1.5x
+# passes (fused and plain) with two query heads per workgroup.  These cases have at least 1.5x
 # that many pairs of short sequences, so that path runs; they cover an odd
 # head count, pairs whose halves belong to different KV heads, fp8, fp32
 # and every head size.
@@ -531,14 +531,19 @@ MANY = [
 
 
 @pytest.mark.parametrize("spec", MANY)
-def test_fused_step_many_short_sequences(gpu_lib, spec):
+@pytest.mark.parametrize("fused", [True, False])
+def test_step_many_short_sequences(gpu_lib, spec, fused):
     n = -(-12288 // spec["hq"])
     lens = np.random.default_rng(11).integers(1, 49, n).tolist()
     case = _custom_case(lens, seed=12, **spec)
-    out, dev = run_fused(case)
+    if fused:
+        out, dev = run_fused(case)
+    else:
+        out, dev = run_step(gpu_lib, case)
     assert_pools_equal_oracle_append(case, dev)
     err = max_err(out, oracle_out(case))
-    print(f"fused, {n} sequences x {spec['hq']} heads: max abs err {err:.3e}")
+    print(f"{'fused' if fused else 'append + decode'}, {n} sequences x "
+          f"{spec['hq']} heads: max abs err {err:.3e}")
     assert err <= TOL[case.config.kv_dtype]
 
 
