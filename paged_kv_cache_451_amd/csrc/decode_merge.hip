@@ -7,7 +7,11 @@
 // One 64-lane workgroup per (sequence, query head).  The partials' (m, l)
 // pairs are read by all lanes at once (lane i takes partial i) and reduced
 // across the wave; the output rows are summed with lane l owning columns
-// d = l + 64 r.
+// d = l + 64 r.  When a batch has more (sequence, query head) pairs than the
+// GPU holds merge workgroups at once, the *_pair_kernel forms run instead:
+// one workgroup per (sequence, pair of query heads), each half of the wave
+// doing the same for one head with 32 lanes (columns d = l + 32 r), so the
+// grid still fits in one round of waves.
 #include <math.h>
 
 #include "pa_launch.h"
