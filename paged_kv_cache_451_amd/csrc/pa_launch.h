@@ -57,7 +57,8 @@ int occupancy_decode_mfma(bool fp8, int head_size);
 int occupancy_decode_valu(int head_size);
 
 // Merge pass over sequences whose blocks were split across ranges;
-// grid = B * Hq workgroups.  out_bf16 selects the output element type.
+// grid = B * Hq workgroups, or B * ceil(Hq / 2) with a.merge_pairs.
+// out_bf16 selects the output element type.
 hipError_t launch_decode_merge(bool out_bf16, int head_size,
                                const DecodeArgs& a, hipStream_t stream);
 // Merge pass of the fused step: every (sequence, query head) combines its
