@@ -45,13 +45,24 @@
 // outside the range, and out-of-range block ids contribute nothing: their
 // scores become -inf and their V values are zeroed in registers, so NaN or
 // stale bytes in unused slots never reach the result.  Such blocks are read
-// from a valid block address (the pair's first block, or block 0).
+// from a valid block address (the pair's first block, or block 0).  A pair
+// that is never computed (the software pipeline's loads past the last pair
+// of the range) reads a zero tile in device memory instead (idle_tile below).
 #include <math.h>
 
 #include "pa_launch.h"
 
 namespace pa {
 namespace {
+
+// Largest (block, KV head) tile the kernel reads: 16 tokens x 256 values of
+// 2 bytes.  Every lane's loads of a pair stay inside one tile (checked at
+// compile time in Pair), so loads pointed at this array with the lanes'
+// tile offsets stay in bounds.  It is read-only and never written: it
+// holds zeros for the whole life of the process, a few lines that stay in
+// the caches.
+constexpr int kIdleTileBytes = 16 * 256 * 2;
+__device__ __align__(256) uint8_t idle_tile[kIdleTileBytes];
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -133,10 +144,25 @@ __device__ __forceinline__ void pair_valid(const RawIds& r, int blk, int hi,
   nv1 = ok1 ? (b > kBlock ? kBlock : (b < 0 ? 0 : b)) : 0;
 }
 
+// Lane-constant element offsets, inside one (block, KV head) tile, of lane
+// (m, j) = (l % 16, l / 16)'s K and V loads (layout at the top of this
+// file): K token row 8*((m/4)%2) + m%4 (MFMA set s adds 4 rows), columns
+// from kColJ * j; V row d = m of the [D][16] tile (each further MFMA adds
+// 16 rows), tokens from 8*(j%2).  Which block of the pair a lane reads is
+// chosen by its base address (m >= 8 for K, j >= 2 for V).
+__host__ __device__ constexpr int k_lane_offset(int r16, int j, int D,
+                                                int col_j) {
+  return (((r16 >> 2) & 1) * 8 + (r16 & 3)) * D + col_j * j;
+}
+__host__ __device__ constexpr int v_lane_offset(int r16, int j) {
+  return r16 * kBlock + 8 * (j & 1);
+}
+
 // Storage-type specific register sets of one pair.  bf16: K chunk c of a row
 // is the 8 values at d = 32c + 8j; fp8: one 16-byte load at d = 64c' + 16j
 // feeds MFMAs 2c' (low 8 bytes) and 2c'+1 (high 8 bytes).  Q uses the same d
-// sets (qcol).
+// sets (qcol).  k_off / v_off give the element offset of each load from the
+// lane's base address, and kKVec / kVVec its width in elements.
 template <bool FP8, int D>
 struct Pair;
 
@@ -144,8 +170,13 @@ template <int D>
 struct Pair<false, D> {
   typedef __bf16 T;
   static constexpr int NC = D / 32, NX = D / 16, kColJ = 8;
+  static constexpr int kKLoads = NC, kKVec = 8, kVVec = 8;
   bf16x8 k[2][NC];
   bf16x8 v[NX];
+  __host__ __device__ static constexpr int k_off(int s, int c) {
+    return 4 * D * s + 32 * c;
+  }
+  __host__ __device__ static constexpr int v_off(int x) { return 256 * x; }
   __device__ static __forceinline__ int qcol(int c, int j) {
     return 32 * c + 8 * j;
   }
@@ -154,11 +185,10 @@ struct Pair<false, D> {
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        k[s][c] = stream_load(
-            reinterpret_cast<const bf16x8*>(kl + 4 * D * s + 32 * c));
+        k[s][c] = stream_load(reinterpret_cast<const bf16x8*>(kl + k_off(s, c)));
 #pragma unroll
     for (int x = 0; x < NX; ++x)
-      v[x] = stream_load(reinterpret_cast<const bf16x8*>(vl + 256 * x));
+      v[x] = stream_load(reinterpret_cast<const bf16x8*>(vl + v_off(x)));
   }
   __device__ __forceinline__ bf16x8 kop(int s, int c) const { return k[s][c]; }
   __device__ __forceinline__ bf16x8 vop(int x) const { return v[x]; }
@@ -168,8 +198,13 @@ template <int D>
 struct Pair<true, D> {
   typedef uint8_t T;
   static constexpr int NC = D / 32, NX = D / 16, kColJ = 16;
+  static constexpr int kKLoads = D / 64, kKVec = 16, kVVec = 8;
   u32x4 k[2][D / 64];
   u32x2 v[NX];
+  __host__ __device__ static constexpr int k_off(int s, int c) {
+    return 4 * D * s + 64 * c;
+  }
+  __host__ __device__ static constexpr int v_off(int x) { return 256 * x; }
   __device__ static __forceinline__ int qcol(int c, int j) {
     return 64 * (c >> 1) + 16 * j + 8 * (c & 1);
   }
@@ -178,11 +213,10 @@ struct Pair<true, D> {
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int c = 0; c < D / 64; ++c)
-        k[s][c] = stream_load(
-            reinterpret_cast<const u32x4*>(kl + 4 * D * s + 64 * c));
+        k[s][c] = stream_load(reinterpret_cast<const u32x4*>(kl + k_off(s, c)));
 #pragma unroll
     for (int x = 0; x < NX; ++x)
-      v[x] = stream_load(reinterpret_cast<const u32x2*>(vl + 256 * x));
+      v[x] = stream_load(reinterpret_cast<const u32x2*>(vl + v_off(x)));
   }
   __device__ __forceinline__ bf16x8 kop(int s, int c) const {
     const u32x4 w = k[s][c >> 1];
@@ -192,6 +226,29 @@ struct Pair<true, D> {
     return fp8x8_to_bf16(v[x][0], v[x][1]);
   }
 };
+
+// True when every load of every lane of a pair stays inside one
+// (block, KV head) tile of 16 * D elements, for K and for V: then a pair
+// read from any valid tile (or from idle_tile) never leaves it.
+template <bool FP8, int D>
+constexpr bool pair_stays_in_tile() {
+  typedef Pair<FP8, D> P;
+  for (int l = 0; l < kWave; ++l) {
+    const int r16 = l & 15, j = l >> 4;
+    const int kb = k_lane_offset(r16, j, D, P::kColJ);
+    for (int s = 0; s < 2; ++s)
+      for (int c = 0; c < P::kKLoads; ++c) {
+        const int o = kb + P::k_off(s, c);
+        if (o < 0 || o + P::kKVec > kBlock * D) return false;
+      }
+    const int vb = v_lane_offset(r16, j);
+    for (int x = 0; x < P::NX; ++x) {
+      const int o = vb + P::v_off(x);
+      if (o < 0 || o + P::kVVec > kBlock * D) return false;
+    }
+  }
+  return kBlock * D * (int)sizeof(typename P::T) <= kIdleTileBytes;
+}
 
 // One sequence b of a workgroup's range: the part [lo, hi) of its blocks
 // that the range covers, its pool length L, and which partial slot it
@@ -246,8 +303,10 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
   const size_t gtile = (size_t)g * tile;
   const size_t btile = (size_t)sc.Hkv * tile;
   // lane-constant parts of the K and V addresses
-  const int k_lane = (((r16 >> 2) & 1) * 8 + (r16 & 3)) * D + P::kColJ * j;
-  const int v_lane = r16 * kBlock + 8 * (j & 1);
+  static_assert(pair_stays_in_tile<FP8, D>(),
+                "a lane's loads must stay inside one (block, head) tile");
+  const int k_lane = k_lane_offset(r16, j, D, P::kColJ);
+  const int v_lane = v_lane_offset(r16, j);
   const bool k_hi = r16 >= 8;  // K row from the pair's second block
   const bool v_hi = j >= 2;    // V tokens from the pair's second block
 
@@ -282,8 +341,10 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
   RawIds ib, ic, id;
   // Loads of pair pblk of the current segment, or, at and past its loop
   // end `blk_end`, of the next segment's pair at nxt.lo + (pblk - blk_end).
-  // A pair past both is never computed: its loads go to the current
-  // sequence's q row (a few lines that are cached anyway) instead of HBM.
+  // A pair past both is never computed: its loads go to idle_tile (a few
+  // cached lines) instead of HBM, at the same lane offsets, which keep them
+  // inside it (pair_stays_in_tile).
+  const T* idle = reinterpret_cast<const T*>(idle_tile);
   auto issue = [&](P& pr, const RawIds& ids, int pblk, const Seg& s,
                    int blk_end) {
     const size_t base0 = (size_t)safe_id(ids.e0, sc.NB) * btile + gtile;
@@ -291,10 +352,8 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
     const bool live =
         pblk < s.hi ||
         (more && pblk >= blk_end && nxt.lo + (pblk - blk_end) < nxt.hi);
-    const T* q_as_t = reinterpret_cast<const T*>(
-        q + ((size_t)s.b * sc.Hq + (size_t)g * G) * D);
-    pr.load(live ? kpool + (k_hi ? base1 : base0) + k_lane : q_as_t,
-            live ? vpool + (v_hi ? base1 : base0) + v_lane : q_as_t);
+    pr.load((live ? kpool + (k_hi ? base1 : base0) : idle) + k_lane,
+            (live ? vpool + (v_hi ? base1 : base0) : idle) + v_lane);
   };
   issue(A, ia, cur.lo, cur, cur.lo + 4);
   ib = raw_ids(trow(cur.b), cur.lo + 2, cur.hi);

@@ -311,3 +311,35 @@ int main(void) {
         r = subprocess.run([exe], capture_output=True, text=True)
         assert r.returncode == 0 and r.stdout.strip() == "ok", \
             (r.returncode, r.stdout, r.stderr)
+
+
+def test_decode_loads_stay_inside_one_tile():
+    """The matrix-core decode kernel reads K/V pairs with lane offsets into
+    one (block, KV head) tile; pairs that are never computed read a zero tile
+    of the same size in device memory.  A compile-time check in the kernel
+    source proves that every lane's loads stay inside one tile for every
+    head size and pool type.  Here two planted mistakes - a zero tile half
+    the size, and K loads shifted past the tile - must each fail the build."""
+    import shutil
+    from paged_kv_cache_451_amd import build as b
+    if not shutil.which(b.HIPCC) and not os.path.exists(b.HIPCC):
+        pytest.skip("hipcc not available")
+    src = open(os.path.join(b.CSRC, "decode_mfma.hip")).read()
+    plants = [
+        ("constexpr int kIdleTileBytes = 16 * 256 * 2;",
+         "constexpr int kIdleTileBytes = 16 * 256;"),
+        ("return 4 * D * s + 32 * c;", "return 4 * D * s + 32 * c + 8;"),
+    ]
+    with tempfile.TemporaryDirectory() as d:
+        for old, new in [(None, None)] + plants:
+            text = src if old is None else src.replace(old, new)
+            assert old is None or text != src, old
+            path = os.path.join(d, "decode_mfma.hip")
+            open(path, "w").write(text)
+            r = subprocess.run([b.HIPCC, *b.CFLAGS, "-fsyntax-only", path],
+                               capture_output=True, text=True)
+            if old is None:
+                assert r.returncode == 0, r.stderr[-2000:]
+            else:
+                assert r.returncode != 0
+                assert "must stay inside one (block, head) tile" in r.stderr
