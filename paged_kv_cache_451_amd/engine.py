@@ -176,19 +176,25 @@ class Engine:
                 break
             req = self.waiting[0]
             ids = req.prompt_ids + req.output_ids
+            # Everything is priced before anything is reserved: the blocks
+            # the admission takes, the blocks the running requests need for
+            # this step's tokens, and one for the request's own first
+            # decoded token when its blocks are full.  A request that does
+            # not fit leaves the pool and the prefix cache untouched (an
+            # admission that registered its fresh blocks in the cache and
+            # was then undone would leave keys to blocks that never
+            # received their KV).
+            take = (self.mgr.blocks_to_admit(ids) if self.prefix_caching
+                    else self.mgr.blocks_needed(len(ids)))
+            grow = 1 if len(ids) % BLOCK_SIZE == 0 else 0
+            if take + self._growth_need() + grow > self.pool.num_free:
+                break
             if self.prefix_caching:
                 ok, hits = self.mgr.admit_cached(req.req_id, ids)
             else:
                 ok, hits = self.mgr.admit(req.req_id, len(ids)), 0
-            if not ok:
-                break
+            assert ok, "an admission that was priced to fit must succeed"
             self.running.append(req)
-            if self._growth_need() > self.pool.num_free:
-                # its first decoded token (or another request's) would not
-                # fit: undo and keep it waiting
-                self.running.pop()
-                self.mgr.free_seq(req.req_id)
-                break
             self.waiting.popleft()
             if req.admitted_step < 0:
                 req.admitted_step = self.step_no

@@ -257,19 +257,12 @@ class KVCacheManager:
         self.req_to_blocks[seq_id] = state
         return True
 
-    def admit_cached(self, seq_id: int,
-                     token_ids: Sequence[int]) -> Tuple[bool, int]:
-        """Admit a request whose tokens are known, reusing cached full
-        blocks of an identical prefix.  Returns (admitted, cached blocks
-        reused); the reused blocks' KV is already in the pool, only the rest
-        must be written.  Fresh full blocks are registered in the cache."""
-        if seq_id in self.req_to_blocks:
-            raise ValueError(f"sequence {seq_id} already admitted")
+    def _cached_prefix(self, toks: Sequence[int]):
+        """Keys of the full blocks of ``toks`` and the cached blocks of its
+        longest cached prefix (lookups stop at the first miss)."""
         bs = self.block_size
-        toks = [int(t) for t in token_ids]
-        nfull = len(toks) // bs
         hashes, parent = [], 0
-        for i in range(nfull):
+        for i in range(len(toks) // bs):
             parent = hash_block_tokens(parent, toks[i * bs:(i + 1) * bs])
             hashes.append(parent)
         hits: List[KVCacheBlock] = []
@@ -278,6 +271,31 @@ class KVCacheManager:
             if blk is None:
                 break
             hits.append(blk)
+        return hashes, hits
+
+    def blocks_to_admit(self, token_ids: Sequence[int]) -> int:
+        """Free-queue blocks ``admit_cached(token_ids)`` would take: its
+        fresh blocks plus the cached hits that sit in the free queue (a
+        touch takes them out of it).  Reserves nothing."""
+        toks = [int(t) for t in token_ids]
+        _, hits = self._cached_prefix(toks)
+        fresh = self.blocks_needed(len(toks)) - len(hits)
+        return fresh + sum(1 for b in hits if b.ref_cnt == 0)
+
+    def admit_cached(self, seq_id: int,
+                     token_ids: Sequence[int]) -> Tuple[bool, int]:
+        """Admit a request whose tokens are known, reusing cached full
+        blocks of an identical prefix.  Returns (admitted, cached blocks
+        reused); the reused blocks' KV is already in the pool, only the rest
+        must be written.  Fresh full blocks are registered in the cache at
+        once, so the caller must write their KV before the next admission
+        can find them (a caller that may undo an admission checks
+        ``blocks_to_admit`` first instead of undoing it)."""
+        if seq_id in self.req_to_blocks:
+            raise ValueError(f"sequence {seq_id} already admitted")
+        toks = [int(t) for t in token_ids]
+        nfull = len(toks) // self.block_size
+        hashes, hits = self._cached_prefix(toks)
         # a hit that sits in the free queue still counts as free until
         # touched: it must not be allocated for this request's fresh blocks
         fresh = self.blocks_needed(len(toks)) - len(hits)
