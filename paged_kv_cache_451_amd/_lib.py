@@ -163,6 +163,70 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+# -- argument checks (before any pointer is taken) ----------------------------
+def _int32(name: str, t: Optional[torch.Tensor], n: Optional[int] = None,
+           ndim: int = 1) -> None:
+    """An index tensor must be int32 (the C ABI reads 32-bit entries; torch's
+    default int64 would be read as pairs of words), with ``ndim`` dimensions
+    and, when given, ``n`` entries along the first."""
+    if t is None:
+        return
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimension(s), "
+                         f"got shape {tuple(t.shape)}")
+    if n is not None and t.shape[0] != n:
+        raise ValueError(f"{name} must have {n} entries along its first "
+                         f"dimension, got {t.shape[0]}")
+
+
+def _pools(k_pool: torch.Tensor, v_pool: torch.Tensor):
+    """Pool shapes: K [NB, Hkv, 16, D] and V [NB, Hkv, D, 16], same dtype."""
+    if k_pool.dim() != 4 or v_pool.dim() != 4:
+        raise ValueError("k_pool and v_pool must be 4-dimensional")
+    nb, hkv, bs, d = k_pool.shape
+    if tuple(v_pool.shape) != (nb, hkv, d, bs):
+        raise ValueError(f"v_pool must have shape {(nb, hkv, d, bs)} "
+                         f"(K's tile transposed), got {tuple(v_pool.shape)}")
+    if v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool and v_pool must have the same dtype")
+    if k_pool.dtype not in _DTYPE:
+        raise ValueError(f"unsupported pool dtype {k_pool.dtype}")
+    return nb, hkv, bs, d
+
+
+def _rows(name: str, t: Optional[torch.Tensor], n: int, hkv: int, d: int,
+          dtype: torch.dtype) -> None:
+    """New-token rows: [n, Hkv, D] of ``dtype``."""
+    if t is None:
+        return
+    if tuple(t.shape) != (n, hkv, d):
+        raise ValueError(f"{name} must have shape {(n, hkv, d)}, got "
+                         f"{tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _check_decode(q, k_pool, v_pool, block_tables, seq_lens, out,
+                  k_new=None, v_new=None, slot_mapping=None) -> None:
+    if q.dim() != 3:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_size]")
+    b, _, d = q.shape
+    nb, hkv, _, d2 = _pools(k_pool, v_pool)
+    if d2 != d:
+        raise ValueError("head_size differs between q and the pools")
+    if q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported q dtype {q.dtype}")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    _int32("block_tables", block_tables, b, ndim=2)
+    _int32("seq_lens", seq_lens, b)
+    _int32("slot_mapping", slot_mapping, b)
+    _rows("k_new", k_new, b, hkv, d, k_pool.dtype)
+    _rows("v_new", v_new, b, hkv, d, k_pool.dtype)
+
+
 def decode_desc(q: torch.Tensor, k_pool: torch.Tensor,
                 block_tables: torch.Tensor, *, max_seq_len: int,
                 k_scale: float = 1.0, v_scale: float = 1.0,
@@ -211,6 +275,7 @@ def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *,
               events: Optional[Sequence] = None,
               desc: Optional[DecodeDesc] = None) -> torch.Tensor:
     """Paged decode attention into ``out`` (see ``include/pa.h``)."""
+    _check_decode(q, k_pool, v_pool, block_tables, seq_lens, out)
     lib = load()
     if desc is None:
         desc = decode_desc(q, k_pool, block_tables, max_seq_len=max_seq_len,
@@ -235,6 +300,8 @@ def pa_decode_append(q, k_pool, v_pool, block_tables, seq_lens, scale, out,
                      desc: Optional[DecodeDesc] = None) -> torch.Tensor:
     """Append of each sequence's newest token fused with decode attention
     over the grown context (see ``include/pa.h``)."""
+    _check_decode(q, k_pool, v_pool, block_tables, seq_lens, out, k_new,
+                  v_new, slot_mapping)
     lib = load()
     if desc is None:
         desc = decode_desc(q, k_pool, block_tables, max_seq_len=max_seq_len,
@@ -261,6 +328,14 @@ def pa_decode_append_shared(q, k_pool, v_pool, block_tables, seq_lens, scale,
                             ) -> torch.Tensor:
     """Cascade form of the fused step: shared prompt prefixes read once per
     group of sequences (see ``include/pa.h``)."""
+    _check_decode(q, k_pool, v_pool, block_tables, seq_lens, out, k_new,
+                  v_new, slot_mapping)
+    if (group_start is None) != (group_prefix_blocks is None):
+        raise ValueError("group_start and group_prefix_blocks go together")
+    if group_start is not None:
+        _int32("group_start", group_start)
+        _int32("group_prefix_blocks", group_prefix_blocks,
+               group_start.numel() - 1)
     lib = load()
     if desc is None:
         desc = decode_desc(q, k_pool, block_tables, max_seq_len=max_seq_len,
@@ -280,8 +355,12 @@ def pa_decode_append_shared(q, k_pool, v_pool, block_tables, seq_lens, scale,
 
 def pa_kv_append(k_new, v_new, slot_mapping, k_pool, v_pool) -> None:
     """Write new tokens' K/V into their pool slots (see ``include/pa.h``)."""
+    _, hkv, _, d = _pools(k_pool, v_pool)
+    n = k_new.shape[0] if k_new.dim() == 3 else -1
+    _rows("k_new", k_new, n, hkv, d, k_pool.dtype)
+    _rows("v_new", v_new, n, hkv, d, k_pool.dtype)
+    _int32("slot_mapping", slot_mapping, n)
     lib = load()
-    n, hkv, d = k_new.shape
     desc = AppendDesc(num_tokens=n, num_kv_heads=hkv, head_size=d,
                       block_size=k_pool.shape[2], num_blocks=k_pool.shape[0],
                       kv_dtype=_DTYPE[k_pool.dtype])
@@ -294,10 +373,14 @@ def pa_kv_append_quant(k_new, v_new, slot_mapping, k_pool, v_pool,
                        k_scale: float, v_scale: float) -> None:
     """Write bf16 rows into an fp8 e4m3fn pool as value / scale codes (see
     ``include/pa.h``)."""
-    lib = load()
-    if k_new.dtype != torch.bfloat16 or k_pool.dtype != torch.float8_e4m3fn:
+    if k_pool.dtype != torch.float8_e4m3fn:
         raise ValueError("pa_kv_append_quant takes bf16 rows and fp8 pools")
-    n, hkv, d = k_new.shape
+    _, hkv, _, d = _pools(k_pool, v_pool)
+    n = k_new.shape[0] if k_new.dim() == 3 else -1
+    _rows("k_new", k_new, n, hkv, d, torch.bfloat16)
+    _rows("v_new", v_new, n, hkv, d, torch.bfloat16)
+    _int32("slot_mapping", slot_mapping, n)
+    lib = load()
     desc = AppendDesc(num_tokens=n, num_kv_heads=hkv, head_size=d,
                       block_size=k_pool.shape[2], num_blocks=k_pool.shape[0],
                       kv_dtype=PA_FP8_E4M3FN)
@@ -310,13 +393,13 @@ def pa_kv_append_quant(k_new, v_new, slot_mapping, k_pool, v_pool,
 def pa_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks) -> None:
     """Copy whole K/V blocks src -> dst (copy-on-write; see
     ``include/pa.h``)."""
+    nb, hkv, bs, d = _pools(k_pool, v_pool)
+    _int32("src_blocks", src_blocks)
+    _int32("dst_blocks", dst_blocks, src_blocks.numel())
     lib = load()
-    nb, hkv, bs, d = k_pool.shape
     desc = CopyDesc(num_pairs=src_blocks.numel(), num_kv_heads=hkv,
                     head_size=d, block_size=bs, num_blocks=nb,
                     kv_dtype=_DTYPE[k_pool.dtype])
-    if dst_blocks.numel() != src_blocks.numel():
-        raise ValueError("src_blocks and dst_blocks differ in length")
     _check(lib.pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(src_blocks),
                               _ptr(dst_blocks), ctypes.byref(desc),
                               _stream()))
@@ -335,6 +418,14 @@ def prefill_desc(q, k_pool, block_tables, num_seqs: int) -> PrefillDesc:
 def pa_prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, scale,
                out, desc: Optional[PrefillDesc] = None) -> torch.Tensor:
     """Chunked-prefill attention into ``out`` (see ``include/pa.h``)."""
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must be [tokens, num_q_heads, head_size] "
+                         "of one dtype")
+    _pools(k_pool, v_pool)
+    b = seq_lens.shape[0] if seq_lens.dim() == 1 else -1
+    _int32("seq_lens", seq_lens, b)
+    _int32("block_tables", block_tables, b, ndim=2)
+    _int32("q_start", q_start, b + 1)
     lib = load()
     if desc is None:
         desc = prefill_desc(q, k_pool, block_tables, seq_lens.numel())
@@ -355,6 +446,13 @@ class PreparedStep:
                  desc: DecodeDesc, workspace: torch.Tensor,
                  k_new=None, v_new=None, slot_mapping=None,
                  fused: bool = False, shared=None):
+        _check_decode(q, k_pool, v_pool, block_tables, seq_lens, out,
+                      k_new if (fused or shared is not None) else None,
+                      v_new if (fused or shared is not None) else None,
+                      slot_mapping if (fused or shared is not None) else None)
+        if shared is not None:
+            _int32("group_start", shared[0])
+            _int32("group_prefix_blocks", shared[1], shared[0].numel() - 1)
         lib = load()
         self._keep = (q, k_pool, v_pool, block_tables, seq_lens, out,
                       workspace, k_new, v_new, slot_mapping, desc, shared)

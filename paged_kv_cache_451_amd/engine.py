@@ -91,9 +91,11 @@ class Engine:
     """Continuous batching over a paged KV pool on one GPU.
 
     ``device=None`` runs the scheduler and block manager only (no kernels),
-    for host-side tests.  ``mirror=True`` keeps a host copy of every K/V
-    value written (and the step's queries) so that each decode can be
-    checked against the oracle.
+    for host-side tests.  ``mirror=True`` records, for the last step, the
+    host copies of every K/V row written with its slots (``last_writes``,
+    in the order the device writes them) and the step's queries, tables and
+    lengths, so that a test can rebuild the pools and check each decode
+    with its own reference.
     """
 
     def __init__(self, num_blocks: int, num_q_heads: int, num_kv_heads: int,
@@ -130,12 +132,10 @@ class Engine:
             self.v_pool = torch.zeros(num_blocks, num_kv_heads, head_size,
                                       BLOCK_SIZE, dtype=torch.bfloat16,
                                       device=device)
-        if mirror:
-            self.k_host = np.zeros((num_blocks, num_kv_heads, BLOCK_SIZE,
-                                    head_size), dtype=np.uint16)
-            self.v_host = np.zeros((num_blocks, num_kv_heads, head_size,
-                                    BLOCK_SIZE), dtype=np.uint16)
-            self.last_q = None
+        # (k rows, v rows, slots) written in the last step, with a mirror:
+        # raw bf16 bits [n, Hkv, D] and int32 slots [n]
+        self.last_writes: List[tuple] = []
+        self.last_q = None
 
     # -- requests ------------------------------------------------------------
     def add_request(self, req: Request) -> None:
@@ -241,7 +241,7 @@ class Engine:
         k, v = self._random_rows(len(slots))
         slots_np = np.asarray(slots, dtype=np.int32)
         if self.mirror:
-            self._mirror_write(k, v, slots)
+            self._record_write(k, v, slots_np)
         if self.device is not None:
             from . import _lib
             t = self.torch
@@ -251,6 +251,7 @@ class Engine:
         return len(slots)
 
     def step(self) -> StepStats:
+        self.last_writes = []
         preempted = self._ensure_growth()
         admitted = self._admit()
         if not self.running and self.waiting:
@@ -309,7 +310,7 @@ class Engine:
             q = self._device_rows(n, "q")
         kn, vn = self._random_rows(n)
         if self.mirror:
-            self._mirror_write(kn, vn, slots)
+            self._record_write(kn, vn, np.asarray(slots, dtype=np.int32))
             self.last_q = q
             self.last_tables, self.last_lens = tables, lens
         if self.device is None:
@@ -342,11 +343,8 @@ class Engine:
                 (e0, e1, int(lens.sum()) * self.hkv * self.d * 2 * 2))
         self.last_out = out
 
-    def _mirror_write(self, k, v, slots) -> None:
+    def _record_write(self, k, v, slots) -> None:
         import torch
-        kb = k.view(torch.uint16).numpy()
-        vb = v.view(torch.uint16).numpy()
-        for i, s in enumerate(slots):
-            p, o = divmod(int(s), BLOCK_SIZE)
-            self.k_host[p, :, o, :] = kb[i]
-            self.v_host[p, :, :, o] = vb[i]
+        self.last_writes.append((k.view(torch.uint16).numpy().copy(),
+                                 v.view(torch.uint16).numpy().copy(),
+                                 np.array(slots, dtype=np.int32)))

@@ -343,3 +343,90 @@ def test_decode_loads_stay_inside_one_tile():
             else:
                 assert r.returncode != 0
                 assert "must stay inside one (block, head) tile" in r.stderr
+
+
+def _decode_tensors(b=3, hq=8, hkv=2, d=64, nb=20, width=4):
+    import torch
+    return dict(
+        q=torch.zeros(b, hq, d, dtype=torch.bfloat16),
+        k_pool=torch.zeros(nb, hkv, 16, d, dtype=torch.bfloat16),
+        v_pool=torch.zeros(nb, hkv, d, 16, dtype=torch.bfloat16),
+        block_tables=torch.zeros(b, width, dtype=torch.int32),
+        seq_lens=torch.ones(b, dtype=torch.int32),
+        out=torch.zeros(b, hq, d, dtype=torch.bfloat16),
+        k_new=torch.zeros(b, hkv, d, dtype=torch.bfloat16),
+        v_new=torch.zeros(b, hkv, d, dtype=torch.bfloat16),
+        slot_mapping=torch.zeros(b, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("field, bad, msg", [
+    ("seq_lens", "int64", "seq_lens must be int32"),
+    ("block_tables", "int64", "block_tables must be int32"),
+    ("slot_mapping", "int64", "slot_mapping must be int32"),
+    ("seq_lens", "short", "seq_lens must have 3 entries"),
+    ("block_tables", "short", "block_tables must have 3 entries"),
+    ("out", "short", "out must have q's shape"),
+    ("out", "f32", "out must have q's shape and dtype"),
+    ("v_pool", "f32", "same dtype"),
+    ("v_pool", "layout", "v_pool must have shape"),
+    ("k_new", "short", "k_new must have shape"),
+    ("v_new", "f32", "v_new must be torch.bfloat16"),
+])
+def test_binding_rejects_wrong_index_types_and_shapes(field, bad, msg):
+    """The binding checks dtypes and shapes before it takes a pointer: an
+    int64 index tensor (torch's default integer type) would otherwise be
+    read as pairs of 32-bit entries."""
+    import torch
+    t = _decode_tensors()
+    x = t[field]
+    if bad == "int64":
+        t[field] = x.to(torch.int64)
+    elif bad == "short":
+        t[field] = x[:-1]
+    elif bad == "f32":
+        t[field] = x.to(torch.float32)
+    elif bad == "layout":
+        t[field] = x.transpose(2, 3).contiguous()
+    with pytest.raises(ValueError, match=msg):
+        _lib.pa_decode_append(t["q"], t["k_pool"], t["v_pool"],
+                              t["block_tables"], t["seq_lens"], 0.1, t["out"],
+                              t["k_new"], t["v_new"], t["slot_mapping"],
+                              max_seq_len=16)
+    if field not in ("k_new", "v_new", "slot_mapping"):
+        with pytest.raises(ValueError, match=msg):
+            _lib.pa_decode(t["q"], t["k_pool"], t["v_pool"],
+                           t["block_tables"], t["seq_lens"], 0.1, t["out"],
+                           max_seq_len=16)
+
+
+def test_binding_rejects_bad_append_copy_and_prefill_indices():
+    import torch
+    t = _decode_tensors()
+    with pytest.raises(ValueError, match="slot_mapping must be int32"):
+        _lib.pa_kv_append(t["k_new"], t["v_new"],
+                          t["slot_mapping"].to(torch.int64), t["k_pool"],
+                          t["v_pool"])
+    with pytest.raises(ValueError, match="dst_blocks must have 2 entries"):
+        _lib.pa_copy_blocks(t["k_pool"], t["v_pool"],
+                            torch.zeros(2, dtype=torch.int32),
+                            torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="src_blocks must be int32"):
+        _lib.pa_copy_blocks(t["k_pool"], t["v_pool"],
+                            torch.zeros(2, dtype=torch.int64),
+                            torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="q_start must have 4 entries"):
+        _lib.pa_prefill(t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+                        t["seq_lens"], torch.zeros(3, dtype=torch.int32), 0.1,
+                        t["out"])
+    with pytest.raises(ValueError, match="group_prefix_blocks must be int32"):
+        _lib.pa_decode_append_shared(
+            t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+            t["seq_lens"], 0.1, t["out"], t["k_new"], t["v_new"],
+            t["slot_mapping"], torch.tensor([0, 3], dtype=torch.int32),
+            torch.tensor([1]), max_seq_len=16)
+    # well-formed CPU tensors get past every check and stop at the device
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        _lib.pa_decode_append(t["q"], t["k_pool"], t["v_pool"],
+                              t["block_tables"], t["seq_lens"], 0.1, t["out"],
+                              t["k_new"], t["v_new"], t["slot_mapping"],
+                              max_seq_len=16)
