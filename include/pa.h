@@ -76,7 +76,9 @@ typedef enum {
   PA_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned */
   PA_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
   PA_ERR_LAUNCH = -6,       /* the HIP runtime rejected a launch */
-  PA_ERR_DEVICE = -7        /* no usable HIP device */
+  PA_ERR_DEVICE = -7,       /* no usable HIP device */
+  PA_ERR_SCRATCH = -8       /* pa_decode_append_noalloc: the call needs more
+                               than the static scratch buffer holds */
 } pa_status;
 
 /*
@@ -201,6 +203,34 @@ int pa_decode_append(const void* q, void* k_pool, void* v_pool,
                      const void* v_new, const int32_t* slot_mapping,
                      const pa_decode_desc* desc, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_append for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, arguments and results, without a workspace
+ * argument.  Its scratch (the contents pa_decode_append keeps in its
+ * workspace) is a static buffer of 32 MiB in the library's device code,
+ * one per device, held from the library's first use on that device until
+ * the process ends.  The call itself allocates nothing.
+ *   Size limit: the call fits when pa_decode_append_workspace_size(desc)
+ *   is at most 32 MiB (33554432 bytes); otherwise it returns
+ *   PA_ERR_SCRATCH and launches nothing.  (About 5 MiB for 64 sequences
+ *   with 32 query heads of size 128, 17 MiB for 256 sequences with 64.)
+ *   Concurrency: every call on one device shares that device's buffer and
+ *   its contents are scratch between calls: calls that overlap on one
+ *   device (unordered streams, or several host threads with different
+ *   streams) race and give undefined results.  Calls ordered on one
+ *   stream are safe.
+ * Errors: as for pa_decode_append (without PA_ERR_WORKSPACE), plus
+ * PA_ERR_SCRATCH, and PA_ERR_DEVICE when the buffer's device address
+ * cannot be resolved.
+ */
+int pa_decode_append_noalloc(const void* q, void* k_pool, void* v_pool,
+                             const int32_t* block_tables,
+                             const int32_t* seq_lens, float scale, void* out,
+                             const void* k_new, const void* v_new,
+                             const int32_t* slot_mapping,
+                             const pa_decode_desc* desc, void* stream);
 
 /*
  * Bytes of workspace that pa_decode_append_shared needs (0 on an invalid

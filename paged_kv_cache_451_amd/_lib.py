@@ -28,7 +28,7 @@ EXPORTS = ("pa_decode", "pa_decode_workspace_size", "pa_decode_append",
            "pa_decode_append_workspace_size", "pa_decode_append_shared",
            "pa_decode_append_shared_workspace_size", "pa_kv_append",
            "pa_kv_append_quant", "pa_copy_blocks", "pa_prefill",
-           "pa_status_string", "pa_abi_version")
+           "pa_status_string", "pa_abi_version", "pa_decode_append_noalloc")
 
 
 class DecodeDesc(ctypes.Structure):
@@ -115,6 +115,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      vp, vp, vp, ctypes.POINTER(DecodeDesc),
                                      vp, sz, vp]
     lib.pa_decode_append.restype = ctypes.c_int
+    lib.pa_decode_append_noalloc.argtypes = [
+        vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
+        ctypes.POINTER(DecodeDesc), vp]
+    lib.pa_decode_append_noalloc.restype = ctypes.c_int
     lib.pa_decode_append_shared_workspace_size.argtypes = [
         ctypes.POINTER(DecodeDesc)]
     lib.pa_decode_append_shared_workspace_size.restype = sz
@@ -315,6 +319,30 @@ def pa_decode_append(q, k_pool, v_pool, block_tables, seq_lens, scale, out,
         _ptr(seq_lens), ctypes.c_float(scale), _ptr(out), _ptr(k_new),
         _ptr(v_new), _ptr(slot_mapping), ctypes.byref(desc), _ptr(workspace),
         workspace.numel(), _stream()))
+    return out
+
+
+def pa_decode_append_noalloc(q, k_pool, v_pool, block_tables, seq_lens,
+                             scale, out, k_new, v_new, slot_mapping, *,
+                             max_seq_len: int, k_scale: float = 1.0,
+                             v_scale: float = 1.0, total_blocks_hint: int = 0,
+                             num_waves: int = 0,
+                             desc: Optional[DecodeDesc] = None
+                             ) -> torch.Tensor:
+    """pa_decode_append with the library's static scratch buffer instead of a
+    workspace: allocates nothing (see ``include/pa.h``)."""
+    _check_decode(q, k_pool, v_pool, block_tables, seq_lens, out, k_new,
+                  v_new, slot_mapping)
+    lib = load()
+    if desc is None:
+        desc = decode_desc(q, k_pool, block_tables, max_seq_len=max_seq_len,
+                           k_scale=k_scale, v_scale=v_scale,
+                           total_blocks_hint=total_blocks_hint,
+                           num_waves=num_waves)
+    _check(lib.pa_decode_append_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        _ptr(seq_lens), ctypes.c_float(scale), _ptr(out), _ptr(k_new),
+        _ptr(v_new), _ptr(slot_mapping), ctypes.byref(desc), _stream()))
     return out
 
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_launch.h"
@@ -39,6 +40,37 @@ int cu_count() {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Scratch of pa_decode_append_noalloc (block prefix sums and split-context
+// partials, the same contents as the workspace of pa_decode_append), for
+// callers that cannot allocate.  Every device the library runs on holds
+// one copy from the time the library's code is loaded on it until the
+// process ends.  Host code never uses the array's name as an address: the
+// device address of each device's copy is resolved once, with that device
+// current, by scratch_on_device().
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch, or nullptr when it
+// cannot be resolved.
+void* scratch_on_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+      return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -358,6 +390,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_DEVICE: return "no usable HIP device";
+    case PA_ERR_SCRATCH:
+      return "call needs more than the library's static scratch buffer";
   }
   return "unknown status";
 }
@@ -400,6 +434,27 @@ int pa_decode_append(const void* q, void* k_pool, void* v_pool,
   return run_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out,
                     k_new, v_new, slot_mapping, k_pool, v_pool, desc,
                     workspace, workspace_bytes, stream);
+}
+
+int pa_decode_append_noalloc(const void* q, void* k_pool, void* v_pool,
+                             const int32_t* block_tables,
+                             const int32_t* seq_lens, float scale, void* out,
+                             const void* k_new, const void* v_new,
+                             const int32_t* slot_mapping,
+                             const pa_decode_desc* desc, void* stream) {
+  if (!desc) return PA_ERR_NULL;
+  if (desc->num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
+    return PA_ERR_NULL;
+  const int st = check_desc(desc);
+  if (st != PA_OK || desc->num_seqs == 0) return st;
+  Plan p;
+  if (!make_plan(desc, true, &p)) return PA_ERR_DEVICE;
+  if (p.bytes > kScratchBytes) return PA_ERR_SCRATCH;
+  void* ws = scratch_on_device();
+  if (!ws) return PA_ERR_DEVICE;
+  return run_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out,
+                    k_new, v_new, slot_mapping, k_pool, v_pool, desc, ws,
+                    kScratchBytes, stream);
 }
 
 size_t pa_decode_append_shared_workspace_size(const pa_decode_desc* desc) {
