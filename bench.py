@@ -10,11 +10,16 @@ like successive layers of a model, so no step finds the previous step's
 blocks in L2 or the Infinity Cache.
 
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (each cached
-token's K and V read once per KV head, q in, out out, table entries, the
-append's read+write) divided by the wall time per step.  ``roofline``
-reports the main decode kernel alone, timed with HIP events recorded on the
-launch stream around it, against the 8 TB/s HBM peak.  ``cpu_baseline`` times
-the float64 CPU oracle on a sample of the same workload.
+token's K and V read once per KV head - for the cascade step on a shared
+prefix, each physical block once - q in, out out, table entries, the
+append's read+write) divided by the wall time per step; the timed region of
+``--steps`` steps runs ``--repeats`` times and ``value`` is the median
+region (min and max beside it).  ``roofline`` reports the main decode
+kernel alone, timed with HIP events recorded on the launch stream around
+it, against the 8 TB/s HBM peak and against the practical ceiling of a plain
+nontemporal read stream of the same byte count, measured in the same run.
+``cpu_baseline`` times the float64 CPU oracle on a sample of the same
+workload, on all cores and on one core.
 """
 from __future__ import annotations
 
@@ -45,8 +50,13 @@ def parse():
     p.add_argument("--num-waves", type=int, default=0)
     p.add_argument("--rotate", type=int, default=0,
                    help="pool copies to rotate over (0: enough for >= 2 GiB)")
+    p.add_argument("--repeats", type=int, default=5,
+                   help="timed regions of --steps steps each; value is the "
+                        "median region, min and max are reported beside it")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="seconds of oracle time per CPU leg (two legs: all "
+                        "cores, then one core)")
     p.add_argument("--unfused", action="store_true",
                    help="time the step as three launches (pa_kv_append, "
                         "then pa_decode) instead of pa_decode_append")
@@ -57,14 +67,20 @@ def parse():
                         "= on for the prefix-shared workload")
     p.add_argument("--op", default="step",
                    choices=["step", "append", "append_quant",
-                            "copy_blocks", "engine", "prefill"],
+                            "copy_blocks", "engine", "prefill", "stream"],
                    help="step: the decode step (default); append / "
                         "append_quant: writing --tokens new tokens into a "
                         "pool (bf16 copy, or bf16 -> fp8 e4m3fn "
                         "quantisation); copy_blocks: copy-on-write of "
                         "--pairs whole blocks; engine: the synthetic "
                         "continuous-batching loop; prefill: chunked-prefill "
-                        "attention (--config prefill_llama3_8b_bf16)")
+                        "attention (--config prefill_llama3_8b_bf16); "
+                        "stream: the practical read ceiling (a plain "
+                        "nontemporal read of --stream-mib MiB) at several "
+                        "grid sizes")
+    p.add_argument("--stream-mib", type=int, default=477,
+                   help="MiB read per launch by --op stream (default: about "
+                        "the decode step's bytes on llama3_8b_bf16)")
     p.add_argument("--pairs", type=int, default=4096,
                    help="block pairs copied per launch by --op copy_blocks")
     p.add_argument("--tokens", type=int, default=32768,
@@ -111,12 +127,40 @@ def measured_traffic(config_name: str, sources=MAIN_KERNEL_SOURCES):
     return int(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(case, budget_s: float):
-    """Float64 oracle over whole sequences until ~budget_s of CPU time."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def _oracle_leg(case, args, budget_s: float):
+    """Whole-sequence oracle decodes in order (cycling) until ~budget_s."""
     import oracle
+    lens = case.seq_lens.numpy()
+    done, t_total, tokens = 0, 0.0, 0
+    while t_total < budget_s:
+        i = done % len(lens)
+        t0 = time.perf_counter()
+        oracle.paged_decode(**args, seqs=[i])
+        t_total += time.perf_counter() - t0
+        done += 1
+        tokens += int(lens[i])
+    return done, tokens, t_total
+
+
+def cpu_baseline(case, budget_s: float):
+    """The float64 oracle, unmodified, on whole sequences of the workload:
+    one leg on every core of the process's affinity mask (BLAS threads as
+    the library sets them), one leg pinned to a single core with one BLAS
+    thread.  KV bytes read per second; the all-core leg is ``value``."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     from oracle.adapters import appended_pools, oracle_args
     from paged_kv_cache_451_amd.workloads import DTYPE_BYTES
 
@@ -124,33 +168,119 @@ def cpu_baseline(case, budget_s: float):
     kp, vp = appended_pools(case)
     args = oracle_args(case)
     args.update(k_raw=kp, v_raw=vp)
-    lens = case.seq_lens.numpy()
-    done, t_total, tokens = [], 0.0, 0
-    while t_total < budget_s:
-        for i in range(len(lens)):
-            t0 = time.perf_counter()
-            oracle.paged_decode(**args, seqs=[i])
-            t_total += time.perf_counter() - t0
-            done.append(i)
-            tokens += int(lens[i])
-            if t_total >= budget_s:
-                break
-    s_kv = DTYPE_BYTES[cfg.kv_dtype]
-    kv_bytes = tokens * cfg.num_kv_heads * cfg.head_size * 2 * s_kv
+    per_token = cfg.num_kv_heads * cfg.head_size * 2 * DTYPE_BYTES[cfg.kv_dtype]
+    cpus = sorted(os.sched_getaffinity(0))
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    done, tokens, t_all = _oracle_leg(case, args, budget_s)
+    # one core: pinned to the first CPU of the mask, one BLAS thread
+    try:
+        os.sched_setaffinity(0, {cpus[0]})
+        with threadpool_limits(limits=1):
+            done1, tokens1, t_one = _oracle_leg(case, args, budget_s)
+    finally:
+        os.sched_setaffinity(0, set(cpus))
+    n = len(case.seq_lens)
     return {
-        "value": round(kv_bytes / t_total / 1e9, 4),
+        "value": round(tokens * per_token / t_all / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": int(min(threads, len(cpus))),
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle, {len(done)} sequence decodes "
-                   f"taken in order (cycling) from the {len(lens)} sequences "
-                   f"of this workload ({tokens} context tokens, "
-                   f"{t_total:.1f} s); KV bytes read per second"),
-        "context_tokens_per_s": round(tokens / t_total, 1),
-        "decode_tokens_per_s": round(len(done) / t_total, 3),
-        "host_cpus": len(os.sched_getaffinity(0)),
+        "sample": (f"float64 numpy oracle, whole-sequence decodes taken in "
+                   f"order (cycling) from the {n} sequences of this "
+                   f"workload: {done} decodes, {tokens} context tokens in "
+                   f"{t_all:.1f} s on {len(cpus)} cores; KV bytes read per "
+                   f"second"),
+        "cpu_model": cpu_model(),
+        "host_cpus": len(cpus),
+        "context_tokens_per_s": round(tokens / t_all, 1),
+        "decode_tokens_per_s": round(done / t_all, 3),
+        "one_core": {
+            "value": round(tokens1 * per_token / t_one / 1e9, 4),
+            "unit": "GB/s", "cores": 1,
+            "sample": (f"the same, pinned to one core with one BLAS thread: "
+                       f"{done1} decodes, {tokens1} context tokens in "
+                       f"{t_one:.1f} s"),
+            "context_tokens_per_s": round(tokens1 / t_one, 1),
+            "decode_tokens_per_s": round(done1 / t_one, 3),
+        },
     }
+
+
+_PROBE = None
+
+
+def _probe_lib():
+    """libpa_probe.so (the practical-ceiling read stream; include/pa_probe.h)."""
+    global _PROBE
+    if _PROBE is None:
+        import ctypes
+        path = os.path.join(ROOT, "paged_kv_cache_451_amd", "libpa_probe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m paged_kv_cache_451_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        lib.pa_probe_read_stream.argtypes = [vp, ctypes.c_size_t, vp,
+                                             ctypes.c_int, vp]
+        lib.pa_probe_read_stream.restype = ctypes.c_int
+        _PROBE = lib
+    return _PROBE
+
+
+def read_ceiling(torch, nbytes: int, grids=(1024, 1536, 2048, 4096), reps=10):
+    """Practical HBM read ceiling: a plain nontemporal read of ``nbytes``
+    (three buffers in turn, so no launch finds its data in the caches),
+    timed with HIP events on the launch stream, at several grid sizes; the
+    best average rate is the ceiling."""
+    import ctypes
+    lib = _probe_lib()
+    n = (nbytes + 15) // 16 * 16
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(i + 1)
+            for i in range(3)]
+    sink = torch.empty(max(grids), dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    rates = {}
+    for grid in grids:
+        def launch(i):
+            st = lib.pa_probe_read_stream(
+                ctypes.c_void_p(bufs[i % 3].data_ptr()), n,
+                ctypes.c_void_p(sink.data_ptr()), grid, sp)
+            if st != 0:
+                raise RuntimeError(f"pa_probe_read_stream failed ({st})")
+        for i in range(3):
+            launch(i)
+        ev = [(torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (e0, e1) in enumerate(ev):
+            e0.record(stream)
+            launch(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+        rates[grid] = n / (ms * 1e-3) / 1e9
+    del bufs, sink
+    best = max(rates, key=rates.get)
+    return {"kind": "nontemporal read stream of the same byte count "
+                    "(libpa_probe.so)",
+            "bytes": n, "achieved": round(rates[best], 2), "unit": "GB/s",
+            "frac_of_peak": round(rates[best] / HBM_PEAK_GBS, 4),
+            "workgroups": best,
+            "by_workgroups": {str(k): round(v, 2) for k, v in rates.items()}}
+
+
+def bench_stream(a, torch):
+    """--op stream: the practical read ceiling on its own line."""
+    c = read_ceiling(torch, a.stream_mib << 20,
+                     grids=(512, 1024, 1536, 2048, 4096, 8192), reps=a.steps)
+    print(json.dumps({
+        "metric": "plain nontemporal HBM read stream: GB/s",
+        "value": c["achieved"], "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": 3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": f"read {a.stream_mib} MiB per launch"},
+        "ceiling": c, "cpu_baseline": None}), flush=True)
 
 
 def copy_calibration(torch):
@@ -568,6 +698,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     _lib.load()
+    if a.op == "stream":
+        bench_stream(a, torch)
+        return
     if a.op == "copy_blocks":
         bench_copy_blocks(a, torch, _lib)
         return
@@ -658,13 +791,20 @@ def main():
     print(f"[bench] warmup done ({a.warmup} steps, {nrot} pool copies)",
           file=sys.stderr, flush=True)
 
-    # the timed region: K whole steps back to back, nothing else on the stream
-    t0 = time.perf_counter()
-    for step in timed:
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / a.steps
+    # The timed regions: each is exactly K whole steps back to back between
+    # two synchronisations, nothing else on the stream; repeated so that the
+    # spread of a short region shows (value = the median region).
+    region_ms = []
+    for _ in range(max(1, a.repeats)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for step in timed:
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        region_ms.append((t1 - t0) * 1e3 / a.steps)
+    ordered = sorted(region_ms)
+    ms_step = ordered[len(ordered) // 2]
 
     # The dominant kernel's duration: the same steps again, each recording a
     # pair of HIP events on the launch stream around its main kernel (around
@@ -681,7 +821,12 @@ def main():
     k_avg = sum(kern_ms) / len(kern_ms)
     k_med = kern_ms[len(kern_ms) // 2]
 
-    value = nbytes["step"] / (ms_step * 1e-3) / 1e9
+    # the step's bytes: each cached token's K and V once per KV head (for
+    # the cascade step, each physical block once: the shared prefix is read
+    # once per group), q, out, table entries, lengths and the append
+    step_bytes = (nbytes["decode_unique"] + nbytes["append"] if cascade
+                  else nbytes["step"])
+    value = step_bytes / (ms_step * 1e-3) / 1e9
     main_bytes = nbytes["main_fused"] if fused else nbytes["decode"]
     kernel_name = ("decode_mfma_kernel" if cfg.kv_dtype != "f32"
                    else "decode_valu_kernel")
@@ -720,10 +865,18 @@ def main():
                      else "pa_kv_append + pa_decode"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "timed_regions": {
+            "repeats": len(region_ms), "steps_each": a.steps,
+            "ms_per_step": [round(x, 5) for x in region_ms],
+            "value_min": round(step_bytes / (ordered[-1] * 1e-3) / 1e9, 2),
+            "value_max": round(step_bytes / (ordered[0] * 1e-3) / 1e9, 2),
+            "pct_of_hbm_peak_min": round(
+                100 * step_bytes / (ordered[-1] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                2)},
         "decode_tokens_per_s": round(cfg.num_seqs / (ms_step * 1e-3), 1),
         "context_tokens_per_s": round(
             nbytes["context_tokens"] / (ms_step * 1e-3), 1),
-        "bytes_per_step": nbytes["step"],
+        "bytes_per_step": step_bytes,
         "roofline": {
             "bound": "hbm",
             "kernel": kernel_name,
@@ -743,8 +896,18 @@ def main():
         "cpu_baseline": None,
     }
     if cfg.lens == "prefix":
+        # every sequence's logical context (the shared prefix counted once
+        # per sequence) over the same step time: not a bandwidth, the
+        # aliased prefix is read once per group
+        res["value_logical_bytes"] = round(
+            nbytes["step"] / (ms_step * 1e-3) / 1e9, 2)
+        res["bytes_per_step_logical"] = nbytes["step"]
         res["roofline"]["achieved_unique"] = round(
             nbytes["decode_unique"] / (k_avg * 1e-3) / 1e9, 2)
+    ceiling = read_ceiling(torch, main_bytes)
+    res["roofline"]["ceiling"] = ceiling
+    res["roofline"]["frac_of_ceiling"] = round(achieved / ceiling["achieved"],
+                                               4)
     if a.copy_calibration:
         copy_calibration(torch)
     if not a.no_cpu_baseline:
