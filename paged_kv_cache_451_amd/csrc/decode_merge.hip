@@ -50,8 +50,8 @@ __device__ __forceinline__ float wave_all(float v) {
             __builtin_bit_cast(float, (unsigned)r32[1]));
 }
 
-// Row of partial `k` (a range index) for sequence span starting at block
-// Sb, or -1 when range k is empty and left no partial.
+// Row of partial `k` (a range index) for the sequence whose span of work
+// units starts at Sb, or -1 when range k is empty and left no partial.
 __device__ __forceinline__ int partial_row(int k, int Sb, int U, int g,
                                            int n, const Sched& s) {
   const int r0 = range_begin(k, U, s.Wh);

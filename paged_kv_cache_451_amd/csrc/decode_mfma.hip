@@ -250,18 +250,25 @@ constexpr bool pair_stays_in_tile() {
   return kBlock * D * (int)sizeof(typename P::T) <= kIdleTileBytes;
 }
 
+// Blocks per work unit of the split schedule (pa_device.h): one loop step,
+// two pairs of blocks.
+constexpr int kUnitShift = 2;
+
 // One sequence b of a workgroup's range: the part [lo, hi) of its blocks
-// that the range covers, its pool length L, and which partial slot it
-// leaves (-1: the range holds all of it, 0: it started in an earlier range,
-// 1: it continues in a later one).
+// that the range covers (its units [Sb, Sb1) clipped to the range's units,
+// in blocks; the sequence's last unit may hold fewer than 4), its pool
+// length L, and which partial slot it leaves (-1: the range holds all of
+// it, 0: it started in an earlier range, 1: it continues in a later one).
 struct Seg {
   int b, lo, hi, L, slot;
   __device__ __forceinline__ void bind(const int32_t* __restrict__ lens,
                                        const Sched& sc, int Sb, int Sb1,
                                        int u0, int u1) {
-    lo = (Sb > u0 ? Sb : u0) - Sb;
-    hi = (Sb1 < u1 ? Sb1 : u1) - Sb;
     L = pool_len(lens[b], sc.len_bias, sc.max_blocks);
+    const int nb = (L + kBlock - 1) / kBlock;
+    lo = ((Sb > u0 ? Sb : u0) - Sb) << kUnitShift;
+    hi = ((Sb1 < u1 ? Sb1 : u1) - Sb) << kUnitShift;
+    hi = hi < nb ? hi : nb;
     slot = Sb < u0 ? 0 : (Sb1 > u1 ? 1 : -1);
   }
 };
@@ -291,8 +298,8 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
   const int k = w / sc.Hkv;
   const int G = sc.G;
 
-  const int U = total_blocks(seq_lens, sc.B, sc.max_blocks, sc.len_bias,
-                             w == 0 ? prefix : nullptr);
+  const int U = total_units(seq_lens, sc.B, sc.max_blocks, sc.len_bias,
+                            kUnitShift, w == 0 ? prefix : nullptr);
   const int u0 = range_begin(k, U, sc.Wh);
   const int u1 = range_begin(k + 1, U, sc.Wh);
   if (u0 >= u1) return;
@@ -313,7 +320,8 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
   // The range's sequences ("segments") in order, one ahead of the one being
   // computed: the last loads a segment issues are the next segment's first
   // pair, so the wave's stream of loads does not stop between sequences.
-  SegCursor cursor(seq_lens, sc.B, sc.max_blocks, sc.len_bias, u0, u1);
+  SegCursor cursor(seq_lens, sc.B, sc.max_blocks, sc.len_bias, kUnitShift,
+                   u0, u1);
   Seg cur, nxt;
   int Sb, Sb1;
   if (!cursor.next(cur.b, Sb, Sb1)) return;

@@ -47,15 +47,16 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
   const int k = w / sc.Hkv;
   const int G = sc.G;
 
-  const int U = total_blocks(seq_lens, sc.B, sc.max_blocks, sc.len_bias,
-                             w == 0 ? prefix : nullptr);
+  // one block per loop step: work units of one block
+  const int U = total_units(seq_lens, sc.B, sc.max_blocks, sc.len_bias, 0,
+                            w == 0 ? prefix : nullptr);
   const int u0 = range_begin(k, U, sc.Wh);
   const int u1 = range_begin(k + 1, U, sc.Wh);
   if (u0 >= u1) return;
 
   const size_t tile = (size_t)kBlock * D;
 
-  for_each_segment(seq_lens, sc.B, sc.max_blocks, sc.len_bias, u0, u1,
+  for_each_segment(seq_lens, sc.B, sc.max_blocks, sc.len_bias, 0, u0, u1,
                    [&](int b, int Sb, int Sb1) {
     const int L = pool_len(seq_lens[b], sc.len_bias, sc.max_blocks);
     const int lo = (Sb > u0 ? Sb : u0) - Sb;

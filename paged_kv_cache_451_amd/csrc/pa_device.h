@@ -1,10 +1,16 @@
 // Device-side helpers shared by the decode kernels of libpa.
 //
 // Work split ("split context"): for every KV head g, the flattened sequence
-// of that head's KV blocks over all sequences (sequence-major, U blocks in
+// of that head's work units over all sequences (sequence-major, U units in
 // total) is cut into Wh equal contiguous ranges, one per 64-lane workgroup.
-// Range k covers blocks [floor(k*U/Wh), floor((k+1)*U/Wh)).  A workgroup
-// walks every sequence that overlaps its range; a sequence wholly inside the
+// A unit is 2^shift consecutive KV blocks of one sequence - the step of the
+// main kernel's loop (4 blocks for the matrix-core kernel, which computes
+// two 2-block pairs per iteration; 1 for the vector kernel) - and a
+// sequence of n blocks has ceil(n / 2^shift) units, its last one possibly
+// partial.  Range k covers units [floor(k*U/Wh), floor((k+1)*U/Wh)), so
+// every range boundary falls on a loop step and ranges cost the same
+// number of steps up to one, whatever the length mix.  A workgroup walks
+// every sequence that overlaps its range; a sequence wholly inside the
 // range is finished in place (its output row written directly), one that
 // crosses a range boundary leaves a partial (running max m, sum l and
 // unnormalised output o) that the merge kernel combines.  Each workgroup
@@ -54,6 +60,14 @@ __device__ __forceinline__ int pool_len(int L, int bias, int max_blocks) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
+// Work units of a sequence of length L (before the bias): its blocks read
+// from the pool, in steps of 2^shift blocks.
+__device__ __forceinline__ int seq_units(int L, int bias, int max_blocks,
+                                         int shift) {
+  const int nb = (pool_len(L, bias, max_blocks) + kBlock - 1) / kBlock;
+  return (nb + (1 << shift) - 1) >> shift;
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = lane_id();
 #pragma unroll
@@ -77,18 +91,17 @@ __device__ __forceinline__ int readlane(int v, int l) {
   return __builtin_amdgcn_readlane(v, l);
 }
 
-// Total blocks U per head (sum of ceil(len/16)); when `prefix` is non-null
+// Total units U per head (the sum of seq_units); when `prefix` is non-null
 // the exclusive prefix is stored for the merge kernel.
-__device__ inline int total_blocks(const int32_t* __restrict__ seq_lens,
-                                   int B, int max_blocks, int bias,
-                                   int32_t* __restrict__ prefix) {
+__device__ inline int total_units(const int32_t* __restrict__ seq_lens,
+                                  int B, int max_blocks, int bias, int shift,
+                                  int32_t* __restrict__ prefix) {
   const int lane = lane_id();
   int carry = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int b = c0 + lane;
     const int nb =
-        b < B ? (pool_len(seq_lens[b], bias, max_blocks) + kBlock - 1) / kBlock
-              : 0;
+        b < B ? seq_units(seq_lens[b], bias, max_blocks, shift) : 0;
     const int incl = wave_incl_scan(nb) + carry;
     if (prefix && b < B) prefix[b] = incl - nb;
     carry = readlane(incl, kWave - 1);
@@ -97,19 +110,18 @@ __device__ inline int total_blocks(const int32_t* __restrict__ seq_lens,
   return carry;
 }
 
-// Calls seg(b, Sb, Sb1) for every sequence b (in order) whose block span
+// Calls seg(b, Sb, Sb1) for every sequence b (in order) whose unit span
 // [Sb, Sb1) overlaps [u0, u1) and is non-empty.  All arguments are uniform.
 template <typename Seg>
 __device__ inline void for_each_segment(const int32_t* __restrict__ seq_lens,
                                         int B, int max_blocks, int bias,
-                                        int u0, int u1, Seg&& seg) {
+                                        int shift, int u0, int u1, Seg&& seg) {
   const int lane = lane_id();
   int carry = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int b = c0 + lane;
     const int nb =
-        b < B ? (pool_len(seq_lens[b], bias, max_blocks) + kBlock - 1) / kBlock
-              : 0;
+        b < B ? seq_units(seq_lens[b], bias, max_blocks, shift) : 0;
     const int incl = wave_incl_scan(nb) + carry;
     const int excl = incl - nb;
     const int chunk_end = readlane(incl, kWave - 1);
@@ -130,25 +142,24 @@ __device__ inline void for_each_segment(const int32_t* __restrict__ seq_lens,
 // can look one segment ahead.  All state is uniform.
 struct SegCursor {
   const int32_t* __restrict__ seq_lens;
-  int B, max_blocks, bias, u0, u1;
+  int B, max_blocks, bias, shift, u0, u1;
   int c0;          // first sequence of the scanned chunk of kWave sequences
-  int chunk_end;   // blocks before the next chunk
-  int excl, incl;  // per lane: block span of sequence c0 + lane
+  int chunk_end;   // units before the next chunk
+  int excl, incl;  // per lane: unit span of sequence c0 + lane
   uint64_t mask;   // lanes of the chunk still to visit
   bool last;       // no later chunk can overlap [u0, u1)
 
   __device__ SegCursor(const int32_t* __restrict__ lens, int B_, int mb,
-                       int bias_, int u0_, int u1_)
-      : seq_lens(lens), B(B_), max_blocks(mb), bias(bias_), u0(u0_),
-        u1(u1_), c0(0), chunk_end(0) {
+                       int bias_, int shift_, int u0_, int u1_)
+      : seq_lens(lens), B(B_), max_blocks(mb), bias(bias_), shift(shift_),
+        u0(u0_), u1(u1_), c0(0), chunk_end(0) {
     scan();
   }
 
   __device__ void scan() {
     const int b = c0 + lane_id();
     const int nb =
-        b < B ? (pool_len(seq_lens[b], bias, max_blocks) + kBlock - 1) / kBlock
-              : 0;
+        b < B ? seq_units(seq_lens[b], bias, max_blocks, shift) : 0;
     incl = wave_incl_scan(nb) + chunk_end;
     excl = incl - nb;
     chunk_end = readlane(incl, kWave - 1);
