@@ -41,8 +41,9 @@
  *
  * Ownership: every array argument is device memory owned by the caller; the
  * library keeps no pointer after a call returns and allocates nothing.
- * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
- * stream) and never synchronise the host.
+ * Calls are asynchronous on `stream` and never synchronise the host.
+ * `stream` is a hipStream_t passed as void* (NULL = the default stream), so
+ * that this header needs no HIP header and plain C programs can include it.
  *
  * Errors: functions return PA_OK (0) or a negative pa_status from host-side
  * checks (null pointers, unsupported shapes or dtypes, misaligned pointers,
@@ -98,14 +99,25 @@ typedef enum {
  *                       (stored value * scale = real value); ignored (use 1)
  *                       for F32/BF16 pools.
  *   total_blocks_hint   sum over b of ceil(seq_lens[b]/16) if the caller
- *                       knows it, else 0; only balances the work split.
- *   num_waves           0 = automatic; else the number of 64-lane
- *                       workgroups of the main kernel (rounded to a multiple
- *                       of num_kv_heads).
- *   profile_events      NULL, or two hipEvent_t the call records on `stream`
- *                       immediately before and after the main kernel (for
- *                       pa_decode_append_shared with groups: before its
- *                       first and after its last launch).
+ *                       knows it, else 0; only sizes the work split (fewer
+ *                       ranges for small batches), never changes a result.
+ *   num_waves           0 = automatic (the recommended setting: one
+ *                       workgroup per range, four per compute unit, in one
+ *                       round); else the number of 64-lane workgroups of the
+ *                       main kernel (rounded down to a multiple of
+ *                       num_kv_heads).  This replaces a per-sequence
+ *                       partition size: the main kernel cuts the flattened
+ *                       work of all sequences into num_waves equal ranges,
+ *                       so no partition length is chosen per sequence.
+ *   reserved            set to 0 (keeps profile_events 8-byte aligned).
+ *   profile_events      a measurement hook, not needed for computing:
+ *                       NULL, or two hipEvent_t the call records on
+ *                       `stream` immediately before and after the main
+ *                       kernel (for pa_decode_append_shared with groups:
+ *                       before its first and after its last launch), so
+ *                       that a benchmark can time the dominant kernel on
+ *                       the stream it runs on.  Recording events serialises
+ *                       the stream; leave both NULL in production calls.
  */
 typedef struct {
   int32_t num_seqs;

@@ -11,6 +11,8 @@
   that stops at the first request that does not fit, and skip-and-continue,
   which admits any later request that still fits.
 """
+import bisect
+import itertools
 import math
 
 
@@ -26,22 +28,26 @@ def contiguous_capacity(pool_blocks, block, max_len):
     return pool_blocks // math.ceil(max_len / block)
 
 
+def _block_needs(block, lens):
+    """Blocks each request takes under paging: ceil(len / block)."""
+    return [-(-int(n) // block) for n in lens]
+
+
 def paged_capacity_fcfs(pool_blocks, block, lens):
-    used = admitted = 0
-    for n in lens:
-        need = math.ceil(n / block)
-        if used + need > pool_blocks:
-            break
-        used += need
-        admitted += 1
-    return admitted, used
+    """First come first served: requests are admitted in order while the
+    running total of their block needs fits in the pool; the first request
+    that would overflow it stops admission.  Returns (admitted, blocks)."""
+    totals = list(itertools.accumulate(_block_needs(block, lens)))
+    admitted = bisect.bisect_right(totals, pool_blocks)
+    return admitted, (totals[admitted - 1] if admitted else 0)
 
 
 def paged_capacity_skip(pool_blocks, block, lens):
-    used = admitted = 0
-    for n in lens:
-        need = math.ceil(n / block)
-        if used + need <= pool_blocks:
-            used += need
-            admitted += 1
-    return admitted, used
+    """Skip-and-continue: a request that does not fit in the blocks still
+    free is passed over and later, smaller requests may still be admitted.
+    Returns (admitted, blocks)."""
+    free, admitted = pool_blocks, []
+    for i, need in enumerate(_block_needs(block, lens)):
+        admitted.append(need <= free)
+        free -= need if admitted[-1] else 0
+    return sum(admitted), pool_blocks - free
