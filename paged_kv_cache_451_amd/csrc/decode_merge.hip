@@ -4,10 +4,11 @@
 // 2^(score - m) and the matching unnormalised output o; with
 // M = max_i m_i and w_i = 2^(m_i - M):
 //     out = sum_i w_i o_i / sum_i w_i l_i.
-// One 64-lane workgroup per (sequence, query head).  The partials' (m, l)
-// pairs are read by all lanes at once (lane i takes partial i) and reduced
-// across the wave; the output rows are summed with lane l owning columns
-// d = l + 64 r.  When a batch has more (sequence, query head) pairs than the
+// One 64-lane wave per (sequence, query head), kMergeWaves waves per
+// workgroup (fewer, larger workgroups dispatch faster; the waves are
+// independent).  The partials' (m, l) pairs are read by all lanes at once
+// (lane i takes partial i) and reduced across the wave; the output rows
+// are summed with lane l owning columns d = l + 64 r.  When a batch has more (sequence, query head) pairs than the
 // GPU holds merge workgroups at once, the *_pair_kernel forms run instead:
 // one workgroup per (sequence, pair of query heads), each half of the wave
 // doing the same for one head with 32 lanes (columns d = l + 32 r), so the
@@ -18,6 +19,21 @@
 
 namespace pa {
 namespace {
+
+// Waves per workgroup of the one-head-per-wave merge kernels (without
+// shared-prefix partials).  Measured on MI355X, fused step of the
+// Llama-shaped batch (2048 waves): 4 per workgroup 86.5 us against 87.3 us
+// with 1; fp8 long-context batch 217.7 against 218.2 us.  The cascade form,
+// which holds the shared partials in registers, stays at 1 (4 was 0.6 us
+// slower).
+constexpr int kMergeWaves = 4;
+
+// The (sequence, query head) row of this wave, or -1 past the last row.
+__device__ __forceinline__ int merge_row(int waves, int rows) {
+  const int r = (int)blockIdx.x * waves +
+                __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  return r < rows ? r : -1;
+}
 
 // Value of lane l ^ 1, l ^ 2 (quad permutations), of the other quad of the
 // lane's 8 (row half-mirror) and of the other 8 of its 16 (row mirror):
@@ -73,7 +89,7 @@ __device__ inline void fold_range_partials(
     float& M, float& lsum, float (&o)[D / 64]) {
   constexpr int NR = D / 64;
   constexpr int kRows = 16;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
   const int np = kl - kf + 1;
   for (int i0 = 0; i0 < np; i0 += kWave) {
     const int cnt = np - i0 < kWave ? np - i0 : kWave;
@@ -120,15 +136,17 @@ __device__ inline void fold_range_partials(
 }
 
 template <typename OT, int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(
+__global__ __launch_bounds__(kWave * kMergeWaves) void decode_merge_kernel(
     OT* __restrict__ out_all, const int32_t* __restrict__ prefix,
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     Sched s) {
   constexpr int NR = D / 64;  // output columns per lane
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
   const int G = s.G;
-  const int n = blockIdx.x % G;
-  const int bg = blockIdx.x / G;
+  const int rid = merge_row(kMergeWaves, s.B * s.Hq);
+  if (rid < 0) return;
+  const int n = rid % G;
+  const int bg = rid / G;
   const int b = bg / s.Hkv;
   const int g = bg % s.Hkv;
   const int Sb = prefix[b];
@@ -201,7 +219,8 @@ struct KvElem<1> {
 // kShared selects the cascade form at compile time, so that the plain step
 // holds no registers for the shared partials.
 template <int KB, int D, bool kShared>
-__global__ __launch_bounds__(64) void decode_merge_append_kernel(
+__global__ __launch_bounds__(kWave * (kShared ? 1 : kMergeWaves)) void
+decode_merge_append_kernel(
     typename KvElem<KB>::io* __restrict__ out_all,
     const typename KvElem<KB>::io* __restrict__ q,
     const int32_t* __restrict__ prefix, const int32_t* __restrict__ seq_lens,
@@ -218,10 +237,12 @@ __global__ __launch_bounds__(64) void decode_merge_append_kernel(
   typedef typename E::io OT;
   typedef typename E::raw RT;
   constexpr int NR = D / 64;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
   const int G = s.G;
-  const int n = blockIdx.x % G;
-  const int bg = blockIdx.x / G;
+  const int rid = merge_row(kShared ? 1 : kMergeWaves, s.B * s.Hq);
+  if (rid < 0) return;
+  const int n = rid % G;
+  const int bg = rid / G;
   const int b = bg / s.Hkv;
   const int g = bg % s.Hkv;
   const size_t h_row = (size_t)b * s.Hq + (size_t)g * G + n;
@@ -591,8 +612,10 @@ void launch_one(const DecodeArgs& a, hipStream_t stream) {
                        a.part_ml, a.part_o, a.s);
     return;
   }
-  const dim3 grid((unsigned)(a.s.B * a.s.Hq));
-  hipLaunchKernelGGL((decode_merge_kernel<OT, D>), grid, dim3(64), 0, stream,
+  const int rows = a.s.B * a.s.Hq;
+  const dim3 grid((unsigned)((rows + kMergeWaves - 1) / kMergeWaves));
+  hipLaunchKernelGGL((decode_merge_kernel<OT, D>), grid,
+                     dim3(kWave * kMergeWaves), 0, stream,
                      reinterpret_cast<OT*>(a.out), a.prefix, a.part_ml,
                      a.part_o, a.s);
 }
@@ -611,9 +634,12 @@ hipError_t launch_m(int head_size, const DecodeArgs& a, hipStream_t stream) {
 template <int KB, int D, bool kShared>
 void launch_append_k(const DecodeArgs& a, hipStream_t stream) {
   typedef KvElem<KB> E;
-  const dim3 grid((unsigned)(a.s.B * a.s.Hq));
+  constexpr int waves = kShared ? 1 : kMergeWaves;
+  const int rows = a.s.B * a.s.Hq;
+  const dim3 grid((unsigned)((rows + waves - 1) / waves));
   hipLaunchKernelGGL(
-      (decode_merge_append_kernel<KB, D, kShared>), grid, dim3(64), 0, stream,
+      (decode_merge_append_kernel<KB, D, kShared>), grid, dim3(kWave * waves),
+      0, stream,
       reinterpret_cast<typename E::io*>(a.out),
       reinterpret_cast<const typename E::io*>(a.q), a.prefix, a.seq_lens,
       a.slots, reinterpret_cast<const typename E::raw*>(a.k_new),
@@ -689,10 +715,10 @@ int occupancy_decode_merge_append(int kv_bytes, int head_size) {
   }
 #undef PA_MERGE_KERNEL
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64, 0) !=
-      hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, f, kWave * kMergeWaves, 0) != hipSuccess)
     return 0;
-  return n;
+  return n * kMergeWaves;
 }
 
 int occupancy_decode_merge(bool out_bf16, int head_size) {
@@ -713,10 +739,10 @@ int occupancy_decode_merge(bool out_bf16, int head_size) {
     default: return 0;
   }
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64, 0) !=
-      hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, f, kWave * kMergeWaves, 0) != hipSuccess)
     return 0;
-  return n;
+  return n * kMergeWaves;
 }
 
 hipError_t launch_decode_merge(bool out_bf16, int head_size,

@@ -349,9 +349,9 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
   if (!cascade && ev[1] && hipEventRecord(ev[1], s) != hipSuccess)
     return PA_ERR_LAUNCH;
   if (fused) {
-    // One query head per merge workgroup while the whole grid fits on the
-    // GPU at once (more loads in flight); two per workgroup beyond that, so
-    // a large batch still takes one round of waves.
+    // One query head per merge wave while the whole grid fits on the GPU
+    // at once (more loads in flight); two per wave beyond that, so a large
+    // batch still takes one round of waves.
     const int kb = (int)dtype_bytes(desc->kv_dtype);
     const int64_t resident =
         (int64_t)pa::occupancy_decode_merge_append(kb, desc->head_size) *

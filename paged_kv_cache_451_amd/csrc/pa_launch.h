@@ -56,8 +56,9 @@ hipError_t launch_decode_valu(int head_size, const DecodeArgs& a,
 int occupancy_decode_mfma(bool fp8, int head_size);
 int occupancy_decode_valu(int head_size);
 
-// Merge pass over sequences whose blocks were split across ranges;
-// grid = B * Hq workgroups, or B * ceil(Hq / 2) with a.merge_pairs.
+// Merge pass over sequences whose blocks were split across ranges; one
+// wave per (sequence, query head), or per (sequence, pair of query heads)
+// with a.merge_pairs.
 // out_bf16 selects the output element type.
 hipError_t launch_decode_merge(bool out_bf16, int head_size,
                                const DecodeArgs& a, hipStream_t stream);
@@ -67,8 +68,8 @@ hipError_t launch_decode_merge(bool out_bf16, int head_size,
 hipError_t launch_decode_merge_append(int kv_bytes, int head_size,
                                       const DecodeArgs& a,
                                       hipStream_t stream);
-// Resident workgroups per compute unit of the fused merge pass with one
-// query head per workgroup (0 on error).
+// Resident waves per compute unit of the fused merge pass with one query
+// head per wave (0 on error).
 int occupancy_decode_merge_append(int kv_bytes, int head_size);
 // The same for the plain merge pass.
 int occupancy_decode_merge(bool out_bf16, int head_size);
