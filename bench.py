@@ -38,6 +38,9 @@ METRIC = ("paged decode attention: achieved HBM GB/s (% of MI355X peak) + "
 ROOT = os.path.dirname(os.path.abspath(__file__))
 MAIN_KERNEL_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "pa_device.h")
 PREFILL_SOURCES = ("prefill_mfma.hip", "pa_device.h", "pa_launch.h")
+# the cascade step's three launches: shared-prefix pass, main pass, merge
+CASCADE_SOURCES = ("decode_mfma.hip", "decode_merge.hip", "prefill_mfma.hip",
+                   "pa_device.h", "pa_launch.h")
 
 
 def parse():
@@ -110,7 +113,8 @@ def kernel_source_hash(sources=MAIN_KERNEL_SOURCES) -> str:
 def measured_traffic(config_name: str, sources=MAIN_KERNEL_SOURCES):
     """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE,
     scaled by a plain copy's counts) from the committed rocprofv3 summary of
-    this workload, or None when the summary is missing or was taken on other
+    this workload (profiles/decode_<name>.md, or profiles/<name>.md for
+    prefill), or None when the summary is missing or was taken on other
     kernel sources."""
     name = config_name if config_name.startswith("prefill") else \
         f"decode_{config_name}"
@@ -837,7 +841,10 @@ def main():
         kernel_name = ("cascade step (suffix tables, shared-prefix pass, "
                        "main pass, merge/append)")
     achieved = main_bytes / (k_avg * 1e-3) / 1e9
-    traffic = None if cascade else measured_traffic(cfg.name)
+    # HBM bytes per launch of the dominant kernel from the committed counter
+    # summary (for the cascade step: per step, over its three launches)
+    traffic = (measured_traffic(f"{cfg.name}_cascade", CASCADE_SOURCES)
+               if cascade else measured_traffic(cfg.name))
     res = {
         "metric": METRIC,
         "value": round(value, 2),
