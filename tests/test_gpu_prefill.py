@@ -4,8 +4,8 @@ Tolerance: max absolute error 2e-2 against the float64 oracle (bf16 q, K,
 V and output; the kernel rounds probabilities to bf16 before the PV
 product, as the decode kernel does).  Reduced cases span many 32-key steps,
 several query tiles per sequence, ragged chunks and ragged last blocks; the
-full-size case runs the benchmark's configuration and compares a sample of
-sequences.
+full-size case runs the benchmark's configuration and compares every output
+element.
 """
 import numpy as np
 import pytest
@@ -81,14 +81,16 @@ def test_prefill_matches_oracle_small(gpu_lib, name, over, chunks):
     assert max_err(out, ref) <= TOL
 
 
-def test_prefill_full_size_sampled(gpu_lib):
+def test_prefill_full_size(gpu_lib):
+    """The benchmark's prefill workload in its launch configuration: every
+    (query token, head, column) against the oracle."""
     case = build_prefill_case(PREFILL_BY_NAME[FULL], seed=0)
     out = run(case)
-    lens = case.seq_lens.numpy()
-    seqs = [int(np.argmin(lens)), int(np.argmax(lens))]
-    ref = oracle.paged_prefill(**prefill_args(case, seqs=seqs))
-    assert max_err(out, ref, rows_of(case, seqs)) <= TOL
-    assert np.isfinite(out.to(torch.float64).numpy()).all()
+    ref = oracle.paged_prefill(**prefill_args(case))
+    err = max_err(out, ref)
+    print(f"prefill full size, all {case.num_tokens} query tokens: max abs "
+          f"err {err:.3e}")
+    assert err <= TOL
 
 
 def test_one_token_chunks_equal_decode(gpu_lib):
