@@ -200,6 +200,58 @@ struct KvElem<1> {
   }
 };
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// The newest token's V column, written as whole rows.  In the [D][16] V
+// tile each row d holds 16 tokens, so the token is one element per row:
+// written alone, that is D isolated stores of 1-4 bytes and a partly
+// written cache line per 4-16 rows, which measured about 3 us per fused step
+// of the Llama-shaped batch (512 columns).  Instead each lane reads its
+// rows d = first + kStride r (all 16 tokens, 16 KB bytes each), replaces
+// token `off` and writes the rows back: consecutive lanes write consecutive
+// rows, so every store instruction covers whole cache lines.  The other 15
+// tokens of each row keep their bytes (the block belongs to this sequence
+// only, and nothing else writes it during the call).
+template <int KB, int D, int kStride>
+struct VRows {
+  typedef typename KvElem<KB>::raw RT;
+  static constexpr int NR = D / kStride;  // rows per lane
+  static constexpr int CH = KB;           // 16-byte chunks per row
+  u32x4 row[NR][CH];
+  __device__ __forceinline__ void load(const RT* v_tile, int first) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          v_tile + (size_t)(first + kStride * r) * kBlock);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) row[r][c] = src[c];
+    }
+  }
+  __device__ __forceinline__ void store(RT* v_tile, int first, int off,
+                                        const RT (&v)[NR]) {
+    constexpr int EPD = 4 / KB;  // elements per dword
+    const int dw = off / EPD;
+    const int shift = 8 * KB * (off % EPD);
+    const unsigned mask =
+        KB == 4 ? 0xFFFFFFFFu : (((1u << (8 * KB)) - 1u) << shift);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const unsigned val = ((unsigned)v[r] << shift) & mask;
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          row[r][c][e] = (4 * c + e == dw)
+                             ? ((row[r][c][e] & ~mask) | val)
+                             : row[r][c][e];
+      u32x4* dst = reinterpret_cast<u32x4*>(
+          v_tile + (size_t)(first + kStride * r) * kBlock);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) dst[c] = row[r][c];
+    }
+  }
+};
+
 // Merge pass of the fused append + decode step, one 64-lane workgroup per
 // (sequence, query head).  The main pass attended to every cached token but
 // the newest one (len_bias = 1) and left partials: range partials for
@@ -278,16 +330,20 @@ decode_merge_append_kernel(
     vr[r] = v_new[kv_row + d];
     qf[r] = (float)q[h_row * D + d];
   }
+  // the wave of the group's first query head writes the token's slot; its
+  // V rows are read with the loads above (one round trip)
+  const bool writes = n == 0 && slot >= 0 && slot < s.NB * kBlock;
+  const size_t tile =
+      writes ? ((size_t)(slot >> 4) * s.Hkv + g) * kBlock * D : 0;
+  VRows<KB, D, kWave> vrows;
+  if (writes) vrows.load(v_pool + tile, lane);
 
-  if (n == 0 && slot >= 0 && slot < s.NB * kBlock) {
-    const size_t tile = ((size_t)(slot >> 4) * s.Hkv + g) * kBlock * D;
+  if (writes) {
     const int off = slot & (kBlock - 1);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int d = lane + 64 * r;
-      k_pool[tile + (size_t)off * D + d] = kr[r];
-      v_pool[tile + (size_t)d * kBlock + off] = vr[r];
-    }
+    for (int r = 0; r < NR; ++r)
+      k_pool[tile + (size_t)off * D + lane + 64 * r] = kr[r];
+    vrows.store(v_pool + tile, lane, off, vr);
   }
 
   float dot = 0.f;
@@ -388,7 +444,7 @@ __device__ inline void fold_range_partials_half(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     float& M, float& lsum, float (&o)[D / 32]) {
   constexpr int NR = D / 32;
-  constexpr int kRows = 8;
+  constexpr int kRows = 4;
   const int il = threadIdx.x & 31;
   const int np = kl - kf + 1;
   for (int i0 = 0; i0 < np; i0 += 32) {
@@ -501,17 +557,12 @@ __global__ __launch_bounds__(64) void decode_merge_append_pair_kernel(
     vr[r] = v_new[kv_row + d];
     qf[r] = (float)q[h_row * D + d];
   }
-
-  if (has_head && n == 0 && slot >= 0 && slot < s.NB * kBlock) {
-    const size_t tile = ((size_t)(slot >> 4) * s.Hkv + g) * kBlock * D;
-    const int off = slot & (kBlock - 1);
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int d = il + 32 * r;
-      k_pool[tile + (size_t)off * D + d] = kr[r];
-      v_pool[tile + (size_t)d * kBlock + off] = vr[r];
-    }
-  }
+  // the half of the group's first query head writes the token's slot, at
+  // the end (V as whole rows): reading the rows up front would hold 32 more
+  // registers through the fold, and this kernel must stay within 64 (8
+  // waves per SIMD, so that the grid runs in one round)
+  const bool writes = has_head && n == 0 && slot >= 0 &&
+                      slot < s.NB * kBlock;
 
   float dot = 0.f;
 #pragma unroll
@@ -551,6 +602,16 @@ __global__ __launch_bounds__(64) void decode_merge_append_pair_kernel(
   OT* out = out_all + h_row * D;
 #pragma unroll
   for (int r = 0; r < NR; ++r) out[il + 32 * r] = (OT)(o[r] * inv);
+  if (writes) {
+    const size_t tile = ((size_t)(slot >> 4) * s.Hkv + g) * kBlock * D;
+    const int off = slot & (kBlock - 1);
+    VRows<KB, D, 32> vrows;
+    vrows.load(v_pool + tile, il);
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      k_pool[tile + (size_t)off * D + il + 32 * r] = kr[r];
+    vrows.store(v_pool + tile, il, off, vr);
+  }
 }
 
 // The plain merge pass with one 64-lane workgroup per (sequence, pair of
