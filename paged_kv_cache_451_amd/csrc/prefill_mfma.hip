@@ -26,9 +26,10 @@
 // (n, h)'s slots of the P^T operand of the PV product.  P never moves
 // between lanes.
 //
-// K/V go through LDS: each step the workgroup copies the four 16-token K
-// tiles ([16][D] each) and V tiles ([D][16] each) of KV head g into one of
-// two LDS buffers while the waves compute on the other.  The copies go from
+// K/V go through LDS: the workgroup copies the four 16-token K tiles
+// ([16][D] each) and V tiles ([D][16] each) of KV head g of a step into
+// one of two K and one of two V buffers while the waves compute on the
+// others (K two steps ahead, V one step ahead).  The copies go from
 // the pool straight into LDS (no registers on the way), wave w copying
 // block w of the step; unpadded rows with XOR-swizzled 16-byte chunks keep
 // the operand reads free of bank conflicts.  Keys at or past the sequence
@@ -36,6 +37,12 @@
 // is zeroed in LDS after the copy lands (a masked probability times them
 // must be 0 even where the slot holds NaN).  The causal mask is applied only
 // on steps that reach past the smallest query position of the wave.
+//
+// Each wave is software-pipelined: while the matrix cores compute step
+// s + 1's scores, the vector unit turns step s's scores into probabilities;
+// while they accumulate step s's PV products, it takes step s + 1's row
+// maxima.  A scheduling fence after every product keeps the two kinds of
+// work interleaved in the instruction stream.
 //
 // The same kernel runs the shared-prefix pass of cascade decode
 // (kShared): a "chunk" is then a group of consecutive decode sequences that
@@ -50,6 +57,8 @@
 // The result is the same in exact arithmetic; only rounding differs.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_launch.h"
 
 namespace pa {
@@ -59,8 +68,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Fourth word of a raw buffer descriptor on gfx9-class GPUs: 32-bit data
+// format, no swizzle, no index stride.
+constexpr int kBufferWord3 = 0x00020000;
 
 constexpr int kPfWaves = kPrefillWaves;
 constexpr int kPfThreads = kPfWaves * kWave;
@@ -92,11 +106,21 @@ __device__ __forceinline__ int kswz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes
-// land at lds + 16 l (lds uniform across the wave).
-__device__ __forceinline__ void copy16_to_lds(const void* src, uint8_t* lds) {
+// One tile of `bytes` bytes at `tile` (uniform) into LDS: instruction m
+// copies 16 bytes per lane from tile + src[m] to dst + 1024 m + 16 lane.
+// The loads go through a buffer descriptor of the tile, so addresses are
+// formed in scalar registers and no load can leave the tile.
+template <int N>
+__device__ __forceinline__ void copy_tile_to_lds(const char* tile, int bytes,
+                                                 const uint32_t (&src)[N],
+                                                 uint8_t* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(tile), 0, bytes, kBufferWord3);
+#pragma unroll
+  for (int m = 0; m < N; ++m)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 1024 * m),
+                                             16, src[m], 0, 0, 0);
 #endif
 }
 
@@ -420,17 +444,17 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
       block_tables + (size_t)(kShared ? qs : b) * sc.max_blocks;
 
   // Block ids: lane u % 4 holds the entry of block 4 s + u % 4 of a step.
-  // They are loaded two steps ahead, so the K/V loads never wait on them.
+  // They are loaded three steps ahead, so the K/V loads never wait on them.
   auto table_entry = [&](int s) -> int {
     const int blk = 4 * s + (lane & 3);
     return trow[blk < nblk ? blk : (nblk > 0 ? nblk - 1 : 0)];
   };
 
-  // Copies go straight from the pool into LDS (global_load_lds_dwordx4:
+  // Copies go straight from the pool into LDS (buffer_load_dwordx4 ... lds:
   // lane l of a wave instruction fills bytes 16 l .. 16 l + 15 of a 1 KiB
-  // LDS span, from any global address it names).  Wave w copies block w of
-  // each step: its K tile as IPT instructions of RPI rows each, and its V
-  // tile as IPT instructions of 32 d rows each.
+  // LDS span, from any offset it names inside the tile).  Wave w copies
+  // block w of each step: its K tile as IPT instructions of RPI rows each,
+  // and its V tile as IPT instructions of 32 d rows each.
   constexpr int CPR = D / 8;             // 16-byte chunks per K row
   constexpr int RPI = kWave / CPR;       // K rows per instruction
   constexpr int IPT = kBlock / RPI;      // instructions per tile
@@ -463,19 +487,25 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
       nvo[u] = ok ? (v > kBlock ? kBlock : v) : 0;
     }
   };
-  // Issues the copies of a step (table entries ids_raw) into buffer buf.
-  auto issue_copies = [&](int buf, int ids_raw) {
+  // Issues the copies of a step's K tiles (table entries ids_raw) into K
+  // buffer buf, and of its V tiles into V buffer buf.  Each wave's copy
+  // reads one 16-token tile through a buffer descriptor built in scalar
+  // registers for that tile, so the per-copy address arithmetic stays off
+  // the vector unit; the lanes' offsets inside the tile are fixed.
+  auto tile_copy = [&](const char* pool, int ids_raw, uint8_t* dst,
+                       const uint32_t (&src)[IPT]) {
     const int raw = readlane(ids_raw, wave);
     const int id = (unsigned)raw < (unsigned)sc.NB ? raw : 0;
-    const char* kb = kp + (size_t)id * blk_stride;  // uniform
-    const char* vb = vp + (size_t)id * blk_stride;
-    uint8_t* kl = lds + buf * Lay::KBytes + kBlock * wave * Lay::KRow;
-    uint8_t* vl = lds + Lay::V0 + buf * Lay::VBytes + wave * Lay::VTile;
-#pragma unroll
-    for (int m = 0; m < IPT; ++m) {
-      copy16_to_lds(kb + k_src[m], kl + 1024 * m);
-      copy16_to_lds(vb + v_src[m], vl + 1024 * m);
-    }
+    copy_tile_to_lds<IPT>(pool + (size_t)id * blk_stride, (int)tile_bytes,
+                          src, dst);
+  };
+  auto issue_k = [&](int buf, int ids_raw) {
+    tile_copy(kp, ids_raw, lds + buf * Lay::KBytes + kBlock * wave * Lay::KRow,
+              k_src);
+  };
+  auto issue_v = [&](int buf, int ids_raw) {
+    tile_copy(vp, ids_raw,
+              lds + Lay::V0 + buf * Lay::VBytes + wave * Lay::VTile, v_src);
   };
   // Zeroes V of tokens at or past nvs[u] in the V tiles of buffer buf (a
   // masked probability times them must be 0, also where the slot holds NaN).
@@ -504,87 +534,176 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   const int k_sw = kswz<D>(n32);  // the same for row 32 + n32
   const int v_off = Lay::V0 + n32 * 32 + 16 * (h ^ ((n32 >> 3) & 1));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  // The two halves' products alternate (independent accumulators back to
-  // back), and the K fragments are read kAhead products ahead.
-  constexpr int kAhead = 4;
-  auto scores = [&](int kbuf, f32x16 sv[2]) {
-    const uint8_t* base = lds + kbuf * Lay::KBytes + k_off;
+  constexpr int NS = 2 * NK;  // score products per step
+  constexpr int NP = 4 * NX;  // PV products per step
+  constexpr int kAhead = 4;   // LDS fragments read this many products ahead
+
+  // K fragment of score product t (d chunk t / 2, key half t % 2) in K
+  // buffer kb; V fragment of PV product t (16-key chunk t / NX, d tile
+  // t % NX) in V buffer vb.
+  auto kfrag = [&](int kb, int t) {
+    const int chunk = (2 * (t >> 1) + h) ^ k_sw;
+    return *reinterpret_cast<const bf16x8*>(
+        lds + kb * Lay::KBytes + k_off + (t & 1) * 32 * Lay::KRow + 16 * chunk);
+  };
+  // K fragment of key half hf, d chunk kc (16 d values) in K buffer kb.
+  auto kfrag_hc = [&](int kb, int hf, int kc) {
+    const int chunk = (2 * kc + h) ^ k_sw;
+    return *reinterpret_cast<const bf16x8*>(
+        lds + kb * Lay::KBytes + k_off + hf * 32 * Lay::KRow + 16 * chunk);
+  };
+  auto vfrag = [&](int vb, int t) {
+    return *reinterpret_cast<const bf16x8*>(
+        lds + vb * Lay::VBytes + v_off + (t / NX) * Lay::VTile +
+        (t % NX) * 32 * 32);
+  };
+  auto zero_scores = [](f32x16 (&sv)[2]) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[hf][i] = 0.f;
-    auto frag = [&](int t) {  // product t: d chunk t / 2, half t % 2
-      const int chunk = (2 * (t >> 1) + h) ^ k_sw;
-      return *reinterpret_cast<const bf16x8*>(base + (t & 1) * 32 * Lay::KRow +
-                                              16 * chunk);
-    };
+  };
+  // Scores of a step on their own (the first step of a tile).
+  auto scores = [&](int kb, f32x16 (&sv)[2]) {
+    zero_scores(sv);
     bf16x8 ring[kAhead];
 #pragma unroll
-    for (int t = 0; t < kAhead; ++t) ring[t] = frag(t);
+    for (int t = 0; t < kAhead; ++t) ring[t] = kfrag(kb, t);
 #pragma unroll
-    for (int t = 0; t < 2 * NK; ++t) {
+    for (int t = 0; t < NS; ++t) {
       const bf16x8 ka = ring[t % kAhead];
-      if (t + kAhead < 2 * NK) ring[t % kAhead] = frag(t + kAhead);
+      if (t + kAhead < NS) ring[t % kAhead] = kfrag(kb, t + kAhead);
       sv[t & 1] = mfma32(ka, qb[t >> 1], sv[t & 1]);
     }
   };
+  // Whether step s needs no mask: four full blocks, all keys at or before
+  // the wave's smallest query position.
+  auto unmasked = [&](int s, const int nv[4]) {
+    return nv[0] == kBlock && nv[1] == kBlock && nv[2] == kBlock &&
+           nv[3] == kBlock && s * kKeys + kKeys - 1 <= wp_min;
+  };
+  // Element pair q (elements 2q, 2q + 1) of a step's scores: -inf past the
+  // row's position or a block's valid tokens.  Element 8c + j of half hf is
+  // key key0 + 32 hf + 16 c + 8 h + j, in block 2 hf + c at offset 8 h + j.
+  auto mask_pair = [&](f32x16 (&sv)[2], int q, int key0, const int nv[4]) {
+    const int hf = q >> 3, c = (q >> 2) & 1, j = 2 * (q & 3);
+    const int lim = pos - (key0 + 32 * hf + 16 * c + 8 * h) + 1;
+    const int nvb = nv[2 * hf + c] - 8 * h;
+    const int thr = lim < nvb ? lim : nvb;
+    sv[hf][8 * c + j] = j < thr ? sv[hf][8 * c + j] : -INFINITY;
+    sv[hf][8 * c + j + 1] = j + 1 < thr ? sv[hf][8 * c + j + 1] : -INFINITY;
+  };
+  auto max_pair = [](const f32x16 (&sv)[2], int q, float mx) {
+    const int hf = q >> 3, e = 2 * (q & 7);
+    mx = fmaxf(mx, sv[hf][e]);
+    return fmaxf(mx, sv[hf][e + 1]);
+  };
+  // Probabilities of element pair q into the P operand, and their sum.
+  // Probabilities of element pair q into the P operand (one packed word of
+  // two bf16), and their sum.
+  auto exp_pair = [&](const f32x16 (&sv)[2], int q, float m_use,
+                      unsigned (&pw)[2][2][4]) {
+    const int hf = q >> 3, c = (q >> 2) & 1, j = 2 * (q & 3);
+    const f32x2 e = {
+        fast_exp2(fmaf(sv[hf][8 * c + j], sc.c_log2, -m_use)),
+        fast_exp2(fmaf(sv[hf][8 * c + j + 1], sc.c_log2, -m_use))};
+    const bf16x2 pp = __builtin_convertvector(e, bf16x2);
+    pw[hf][c][j >> 1] = __builtin_bit_cast(unsigned, pp);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+  };
+  // The P operand of 16-key chunk ch.
+  auto p_operand = [](const unsigned (&pw)[2][2][4], int ch) {
+    const u32x4 w = {pw[ch >> 1][ch & 1][0], pw[ch >> 1][ch & 1][1],
+                     pw[ch >> 1][ch & 1][2], pw[ch >> 1][ch & 1][3]};
+    return __builtin_bit_cast(bf16x8, w);
+  };
 
-  int nv_cur[4] = {0, 0, 0, 0};
-  int ids_next = 0;  // table entries of the next copy
+  // The phases below are written as groups of one product, its share of
+  // the vector work and the LDS read of a later fragment; a scheduling
+  // fence after each group keeps that order, so that the matrix cores and
+  // the vector unit work side by side and no fragment is read far ahead.
+  auto fence = []() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+  };
+
+  // Software pipeline.  Iteration s turns step s's scores into
+  // probabilities while the matrix cores compute step s + 1's scores, then
+  // accumulates step s's PV products while the vector unit masks step
+  // s + 1's scores and takes their row maxima: each wave keeps its own
+  // products and vector work in flight together.  K therefore runs one step
+  // ahead of V: iteration s copies K of step s + 2 (into the buffer that
+  // held K of step s) and V of step s + 1, and both land behind the
+  // iteration's closing barrier.
+  int nv_nxt[4] = {0, 0, 0, 0};
+  // scores of the current and the next step, in two register sets that
+  // swap roles from step to step (the loop is unrolled by two)
+  f32x16 s_a[2], s_b[2];
+  zero_scores(s_a);
+  float m_cand = -INFINITY;  // step s's row maximum (log2 units)
+  int e1 = 0, e2 = 0;        // table entries of steps s + 1 and s + 2
   const int last = s_end - 1;
   if (s_end > s_begin) {
     const int e0 = table_entry(s_begin);
-    issue_copies(0, e0);
-    valid_of(s_begin, e0, nv_cur);
-    ids_next = table_entry(last < s_begin + 1 ? last : s_begin + 1);
+    e1 = table_entry(last < s_begin + 1 ? last : s_begin + 1);
+    issue_k(0, e0);
+    issue_v(0, e0);
+    if (last > s_begin) issue_k(1, e1);
+    int nv0[4];
+    valid_of(s_begin, e0, nv0);
+    e2 = table_entry(last < s_begin + 2 ? last : s_begin + 2);
     wait_all_memory();
     __syncthreads();
-    if (partial(nv_cur)) {
-      zero_v_tail(0, nv_cur);
+    if (partial(nv0)) {
+      zero_v_tail(0, nv0);
       __syncthreads();
     }
-  }
-
-  // Double-buffered steps: while the waves compute on step s (buffer
-  // s & 1), the copies of step s + 1 into the other buffer are in flight;
-  // each step ends by waiting for them and a barrier (and, when a block of
-  // the next step is partly valid, zeroing its V tail behind one more).
-  for (int s = s_begin; s < s_end; ++s) {
-    const bool more = s < last;
-    const int buf = (s - s_begin) & 1;
-    int nv_next[4];
-    if (more) issue_copies(buf ^ 1, ids_next);
-    valid_of(more ? s + 1 : s, ids_next, nv_next);
-    ids_next = table_entry(s + 2 < last ? s + 2 : last);
-
-    f32x16 s_cur[2];
-    scores(buf, s_cur);
-    const int key0 = s * kKeys;
-    const bool full = nv_cur[0] == kBlock && nv_cur[1] == kBlock &&
-                      nv_cur[2] == kBlock && nv_cur[3] == kBlock &&
-                      key0 + kKeys - 1 <= wp_min;
-    if (!full) {
-      // element 8c + j of half hf: key key0 + 32 hf + 16 c + 8 h + j, in
-      // block 2 hf + c at offset 8 h + j
+    scores(0, s_a);
+    if (!unmasked(s_begin, nv0)) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int lim = pos - (key0 + 32 * hf + 16 * c + 8 * h);
-          const int nvb = nv_cur[2 * hf + c] - 8 * h;
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            s_cur[hf][8 * c + j] =
-                (j <= lim && j < nvb) ? s_cur[hf][8 * c + j] : -INFINITY;
-        }
+      for (int q = 0; q < 16; ++q) mask_pair(s_a, q, s_begin * kKeys, nv0);
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+    for (int q = 0; q < 16; ++q) mx = max_pair(s_a, q, mx);
+    m_cand = max_xor32(mx) * sc.c_log2;
+    __syncthreads();  // K buffer 0 is refilled by the first iteration
+  }
+
+  // PV products of step s from V buffer vb, with `extra(t)` (vector work
+  // on the next step's scores) after product t.
+  auto pv_products = [&](int vb, const unsigned (&pw)[2][2][4], auto extra) {
+    bf16x8 vring[kAhead];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[hf][i]);
-    mx = max_xor32(mx);
-    const float m_cand = mx * sc.c_log2;
+    for (int t = 0; t < kAhead; ++t) vring[t] = vfrag(vb, t);
+#pragma unroll
+    for (int t = 0; t < NP; ++t) {
+      const bf16x8 va = vring[t % kAhead];
+      if (t + kAhead < NP) vring[t % kAhead] = vfrag(vb, t + kAhead);
+      const int ch = t / NX;
+      acc[t % NX] = mfma32(va, p_operand(pw, ch), acc[t % NX]);
+      extra(t);
+      fence();
+    }
+  };
+
+  // One step: s_cur holds its scores, s_nxt receives step s + 1's; cb_tag
+  // is (s - s_begin) & 1, the buffer pair it reads; kMore: step s + 1
+  // exists (its scores are computed here).
+  auto step = [&](int s, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], auto cb_tag,
+                  auto more_tag) {
+    constexpr bool kMore = decltype(more_tag)::value;
+    constexpr int cb = decltype(cb_tag)::value, nb = cb ^ 1;
+    // the table entries of step s + 3 are loaded before this step's copies
+    // are issued, so that waiting for them leaves the copies in flight
+    const int e3 = table_entry(s + 3 < last ? s + 3 : last);
+    if (kMore) {
+      if (s + 2 <= last) issue_k(cb, e2);
+      issue_v(nb, e1);
+      valid_of(s + 1, e1, nv_nxt);
+    }
+
     // rescale when some row's max grew by more than kLazy (or was unset)
     if (__ballot(m_cand > m_run + kLazy ||
                  (m_run == -INFINITY && m_cand > -INFINITY))) {
@@ -597,48 +716,79 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
       m_run = m_new;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    bf16x8 pb[2][2];
+
+    unsigned pw[2][2][4];
+    if constexpr (!kMore) {
+      // last step: probabilities, then the PV products
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+      for (int q = 0; q < 16; ++q) exp_pair(s_cur, q, m_use, pw);
+      pv_products(cb, pw, [](int) {});
+    } else {
+      // Phase A: probabilities of step s, scores of step s + 1, one key
+      // half after the other (each half's scores die as the next step's
+      // accumulator of that half fills).
+      {
+        constexpr int kPer = 16 / NS;  // probability pairs per product
+        bf16x8 ring[kAhead];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+        for (int t = 0; t < kAhead; ++t) ring[t] = kfrag_hc(nb, t / NK, t % NK);
+        fence();
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const __bf16 p0 = (__bf16)fast_exp2(
-              fmaf(s_cur[hf][8 * c + j], sc.c_log2, -m_use));
-          const __bf16 p1 = (__bf16)fast_exp2(
-              fmaf(s_cur[hf][8 * c + j + 1], sc.c_log2, -m_use));
-          pb[hf][c][j] = p0;
-          pb[hf][c][j + 1] = p1;
-          const bf16x2 pp = {p0, p1};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+        for (int t = 0; t < NS; ++t) {
+          const int hf = t / NK, kc = t % NK;
+          const bf16x8 ka = ring[t % kAhead];
+          if (t + kAhead < NS)
+            ring[t % kAhead] =
+                kfrag_hc(nb, (t + kAhead) / NK, (t + kAhead) % NK);
+          const f32x16 zero = {};
+          s_nxt[hf] = mfma32(ka, qb[kc], kc == 0 ? zero : s_nxt[hf]);
+#pragma unroll
+          for (int u = 0; u < kPer; ++u)
+            exp_pair(s_cur, t * kPer + u, m_use, pw);
+          fence();
         }
-    // products: 16-key chunk outer, d tile inner (independent
-    // accumulators back to back), V fragments read kAhead ahead
-    const uint8_t* vbase = lds + buf * Lay::VBytes + v_off;
-    auto vfrag = [&](int t) {  // product t: chunk t / NX, d tile t % NX
-      const int ch = t / NX, X = t % NX;
-      return *reinterpret_cast<const bf16x8*>(vbase + ch * Lay::VTile +
-                                              X * 32 * 32);
-    };
-    bf16x8 vring[kAhead];
+      }
+      // Phase B: PV products of step s; row maxima of step s + 1 (after
+      // its mask, on the rare steps that need one).
+      float mx = -INFINITY;
+      if (unmasked(s + 1, nv_nxt)) {
+        pv_products(cb, pw, [&](int t) {
 #pragma unroll
-    for (int t = 0; t < kAhead; ++t) vring[t] = vfrag(t);
+          for (int u = 0; u < 16 / NP; ++u)
+            mx = max_pair(s_nxt, t * (16 / NP) + u, mx);
+        });
+      } else {
+        pv_products(cb, pw, [](int) {});
 #pragma unroll
-    for (int t = 0; t < 4 * NX; ++t) {
-      const bf16x8 va = vring[t % kAhead];
-      if (t + kAhead < 4 * NX) vring[t % kAhead] = vfrag(t + kAhead);
-      const int ch = t / NX;
-      acc[t % NX] = mfma32(va, pb[ch >> 1][ch & 1], acc[t % NX]);
-    }
-    wait_all_memory();
-    __syncthreads();
-    if (more && partial(nv_next)) {
-      zero_v_tail(buf ^ 1, nv_next);
+        for (int q = 0; q < 16; ++q) {
+          mask_pair(s_nxt, q, (s + 1) * kKeys, nv_nxt);
+          mx = max_pair(s_nxt, q, mx);
+        }
+      }
+      m_cand = max_xor32(mx) * sc.c_log2;
+
+      wait_all_memory();
       __syncthreads();
+      if (partial(nv_nxt)) {
+        zero_v_tail(nb, nv_nxt);
+        __syncthreads();
+      }
+      e1 = e2;
+      e2 = e3;
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) nv_cur[u] = nv_next[u];
+  };
+  typedef std::integral_constant<int, 0> Buf0;
+  typedef std::integral_constant<int, 1> Buf1;
+  int s = s_begin;
+  for (; s + 1 < last; s += 2) {
+    step(s, s_a, s_b, Buf0(), std::true_type());
+    step(s + 1, s_b, s_a, Buf1(), std::true_type());
+  }
+  if (s < last) {
+    step(s, s_a, s_b, Buf0(), std::true_type());
+    step(last, s_b, s_a, Buf1(), std::false_type());
+  } else if (s == last) {
+    step(last, s_a, s_b, Buf0(), std::false_type());
   }
 
   // lane (n, h) holds O[row n][32 X + 8 a + 4 h + i] in element 4 a + i
