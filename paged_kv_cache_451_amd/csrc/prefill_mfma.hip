@@ -536,7 +536,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   constexpr int NS = 2 * NK;  // score products per step
   constexpr int NP = 4 * NX;  // PV products per step
-  constexpr int kAhead = 4;   // LDS fragments read this many products ahead
+  // LDS fragments are read this many products ahead (fewer in the
+  // shared-prefix pass, whose partial outputs need more registers)
+  constexpr int kAhead = kShared ? 2 : 4;
 
   // K fragment of score product t (d chunk t / 2, key half t % 2) in K
   // buffer kb; V fragment of PV product t (16-key chunk t / NX, d tile
