@@ -726,22 +726,22 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
       for (int q = 0; q < 16; ++q) exp_pair(s_cur, q, m_use, pw);
       pv_products(cb, pw, [](int) {});
     } else {
-      // Phase A: probabilities of step s, scores of step s + 1, one key
-      // half after the other (each half's scores die as the next step's
-      // accumulator of that half fills).
+      // Phase A: probabilities of step s, scores of step s + 1 (the two key
+      // halves' products alternate, so that back-to-back products use
+      // independent accumulators).
       {
         constexpr int kPer = 16 / NS;  // probability pairs per product
         bf16x8 ring[kAhead];
 #pragma unroll
-        for (int t = 0; t < kAhead; ++t) ring[t] = kfrag_hc(nb, t / NK, t % NK);
+        for (int t = 0; t < kAhead; ++t) ring[t] = kfrag_hc(nb, t & 1, t >> 1);
         fence();
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
-          const int hf = t / NK, kc = t % NK;
+          const int hf = t & 1, kc = t >> 1;
           const bf16x8 ka = ring[t % kAhead];
           if (t + kAhead < NS)
             ring[t % kAhead] =
-                kfrag_hc(nb, (t + kAhead) / NK, (t + kAhead) % NK);
+                kfrag_hc(nb, (t + kAhead) & 1, (t + kAhead) >> 1);
           const f32x16 zero = {};
           s_nxt[hf] = mfma32(ka, qb[kc], kc == 0 ? zero : s_nxt[hf]);
 #pragma unroll
