@@ -186,3 +186,15 @@ def test_shared_prompts_other_head_shapes(hq, hkv, d):
     out, dev = run_shared(case, groups, pb, tables=tab)
     assert max_err(out, oracle_ref(case, tables=tab)) <= TOL
     assert_pools_appended(case, dev)
+
+
+@pytest.mark.parametrize("prefix_len", [16, 64, 80, 192, 208, 1040])
+def test_shared_prefix_step_counts(prefix_len):
+    """Prefixes of 1 to 17 64-key steps: the shared-prefix pass's two-step
+    loop runs with odd and even step counts in every key range."""
+    cfg = CONFIG_BY_NAME["prefix_shared_bf16"].replace(
+        num_seqs=6, prefix_len=prefix_len, lo=1, hi=100)
+    case = build_case(cfg, 5)
+    out, dev = run_shared(case, [0, cfg.num_seqs], [prefix_len // 16])
+    assert max_err(out, oracle_ref(case)) <= TOL
+    assert_pools_appended(case, dev)

@@ -2,7 +2,7 @@
 
 Tolerance: max absolute error 2e-2 against the float64 oracle (bf16 q, K,
 V and output; the kernel rounds probabilities to bf16 before the PV
-product, as the decode kernel does).  Reduced cases span many 32-key steps,
+product, as the decode kernel does).  Reduced cases span many 64-key steps,
 several query tiles per sequence, ragged chunks and ragged last blocks; the
 full-size case runs the benchmark's configuration and compares every output
 element.
@@ -69,6 +69,13 @@ SMALL = [
                      head_size=64, prior_lo=100, prior_hi=700), [20, 57]),
     ("g2_d128", dict(num_seqs=2, num_q_heads=4, num_kv_heads=2,
                      prior_lo=1, prior_hi=50), [16, 200]),
+    # whole prompts ending at and just past 64-key step boundaries: tiles
+    # that take 1 to 5 steps, so the kernel's two-step loop runs with an
+    # odd and an even number of steps, with and without a full pair
+    ("step_edges", dict(num_seqs=9, prior_lo=0, prior_hi=0),
+     [1, 64, 65, 128, 129, 192, 193, 256, 320]),
+    ("step_edges_d64", dict(num_seqs=6, head_size=64, prior_lo=0,
+                            prior_hi=0), [63, 64, 65, 127, 191, 257]),
 ]
 
 
