@@ -231,6 +231,44 @@ __device__ void tile_of_rank(const int32_t* __restrict__ q_start,
                              int* t_out) {
   *b_out = -1;
   *t_out = 0;
+  if (sc.B <= kWave) {
+    // Up to one sequence per lane: the sequences' chunks are loaded once
+    // and every count of the search below runs on registers (with loads in
+    // each count, the search's dependent round trips cost a few
+    // microseconds per tile).
+    const int lane = lane_id();
+    const bool live = lane < sc.B;
+    const Chunk c =
+        live ? chunk_of<kShared>(q_start, seq_lens, lane, sc) : Chunk{0, 0, 0};
+    auto count = [&](int W) {
+      return wave_sum(live ? tiles_at_least<kShared>(c, sc.G, W) : 0);
+    };
+    if (r >= count(0)) return;
+    int lo = 0, hi = (sc.max_blocks * kBlock + kKeys - 1) / kKeys + 1;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (count(mid) > r)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int W = lo;
+    const int k = r - count(W + 1);
+    int eq = 0, first = 0;
+    if (live) {
+      const int ge = tiles_at_least<kShared>(c, sc.G, W);
+      eq = ge - tiles_at_least<kShared>(c, sc.G, W + 1);
+      first = tiles_of(c, sc.G) - ge;
+    }
+    const int incl = wave_incl_scan(eq);
+    const uint64_t hit = __ballot(eq > 0 && k < incl && k >= incl - eq);
+    if (hit) {
+      const int i = __builtin_ctzll(hit);
+      *b_out = i;
+      *t_out = readlane(first, i) + k - (readlane(incl, i) - readlane(eq, i));
+    }
+    return;
+  }
   if (r >= count_at_least<kShared>(q_start, seq_lens, sc, 0)) return;
   // largest W with count_at_least(W) > r
   int lo = 0, hi = (sc.max_blocks * kBlock + kKeys - 1) / kKeys + 1;

@@ -76,6 +76,9 @@ SMALL = [
      [1, 64, 65, 128, 129, 192, 193, 256, 320]),
     ("step_edges_d64", dict(num_seqs=6, head_size=64, prior_lo=0,
                             prior_hi=0), [63, 64, 65, 127, 191, 257]),
+    # more sequences than a wave has lanes: the tile search's general path
+    ("many_seqs", dict(num_seqs=70, prior_lo=0, prior_hi=150),
+     [1 + (7 * i) % 40 for i in range(70)]),
 ]
 
 
