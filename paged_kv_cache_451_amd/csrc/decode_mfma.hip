@@ -298,8 +298,10 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
   const int k = w / sc.Hkv;
   const int G = sc.G;
 
+  int first_units;
   const int U = total_units(seq_lens, sc.B, sc.max_blocks, sc.len_bias,
-                            kUnitShift, w == 0 ? prefix : nullptr);
+                            kUnitShift, w == 0 ? prefix : nullptr,
+                            &first_units);
   const int u0 = range_begin(k, U, sc.Wh);
   const int u1 = range_begin(k + 1, U, sc.Wh);
   if (u0 >= u1) return;
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
   // computed: the last loads a segment issues are the next segment's first
   // pair, so the wave's stream of loads does not stop between sequences.
   SegCursor cursor(seq_lens, sc.B, sc.max_blocks, sc.len_bias, kUnitShift,
-                   u0, u1);
+                   u0, u1, first_units);
   Seg cur, nxt;
   int Sb, Sb1;
   if (!cursor.next(cur.b, Sb, Sb1)) return;

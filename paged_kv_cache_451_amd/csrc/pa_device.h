@@ -93,19 +93,25 @@ __device__ __forceinline__ int readlane(int v, int l) {
 
 // Total units U per head (the sum of seq_units); when `prefix` is non-null
 // the exclusive prefix is stored for the merge kernel.
+// `first` (optional) receives this lane's units of sequence `lane` (the
+// first chunk of kWave sequences), so that a cursor over the same
+// sequences need not load them again.
 __device__ inline int total_units(const int32_t* __restrict__ seq_lens,
                                   int B, int max_blocks, int bias, int shift,
-                                  int32_t* __restrict__ prefix) {
+                                  int32_t* __restrict__ prefix,
+                                  int* first = nullptr) {
   const int lane = lane_id();
   int carry = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int b = c0 + lane;
     const int nb =
         b < B ? seq_units(seq_lens[b], bias, max_blocks, shift) : 0;
+    if (first && c0 == 0) *first = nb;
     const int incl = wave_incl_scan(nb) + carry;
     if (prefix && b < B) prefix[b] = incl - nb;
     carry = readlane(incl, kWave - 1);
   }
+  if (first && B <= 0) *first = 0;
   if (prefix && lane == 0) prefix[B] = carry;
   return carry;
 }
@@ -149,17 +155,21 @@ struct SegCursor {
   uint64_t mask;   // lanes of the chunk still to visit
   bool last;       // no later chunk can overlap [u0, u1)
 
+  // first: this lane's units of sequence `lane`, as total_units returns
+  // them (the first chunk is then not loaded again)
   __device__ SegCursor(const int32_t* __restrict__ lens, int B_, int mb,
-                       int bias_, int shift_, int u0_, int u1_)
+                       int bias_, int shift_, int u0_, int u1_, int first)
       : seq_lens(lens), B(B_), max_blocks(mb), bias(bias_), shift(shift_),
         u0(u0_), u1(u1_), c0(0), chunk_end(0) {
-    scan();
+    scan_units(first);
   }
 
   __device__ void scan() {
     const int b = c0 + lane_id();
-    const int nb =
-        b < B ? seq_units(seq_lens[b], bias, max_blocks, shift) : 0;
+    scan_units(b < B ? seq_units(seq_lens[b], bias, max_blocks, shift) : 0);
+  }
+
+  __device__ void scan_units(int nb) {
     incl = wave_incl_scan(nb) + chunk_end;
     excl = incl - nb;
     chunk_end = readlane(incl, kWave - 1);
