@@ -211,7 +211,10 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // token `off` and writes the rows back: consecutive lanes write consecutive
 // rows, so every store instruction covers whole cache lines.  The other 15
 // tokens of each row keep their bytes (the block belongs to this sequence
-// only, and nothing else writes it during the call).
+// only, and nothing else writes it during the call).  The stores, and those
+// of the token's K row, are nontemporal: nothing reads the lines before the
+// next step's main pass streams them from HBM (measured: 0.2 us less per
+// step of the Llama-shaped batch, 0.5 us on the 256-sequence one).
 template <int KB, int D, int kStride>
 struct VRows {
   typedef typename KvElem<KB>::raw RT;
@@ -247,7 +250,7 @@ struct VRows {
       u32x4* dst = reinterpret_cast<u32x4*>(
           v_tile + (size_t)(first + kStride * r) * kBlock);
 #pragma unroll
-      for (int c = 0; c < CH; ++c) dst[c] = row[r][c];
+      for (int c = 0; c < CH; ++c) __builtin_nontemporal_store(row[r][c], dst + c);
     }
   }
 };
@@ -366,7 +369,7 @@ decode_merge_append_kernel(
     const int off = slot & (kBlock - 1);
 #pragma unroll
     for (int r = 0; r < NR; ++r)
-      k_pool[tile + (size_t)off * D + lane + 64 * r] = kr[r];
+      __builtin_nontemporal_store(kr[r], k_pool + tile + (size_t)off * D + lane + 64 * r);
     vrows.store(v_pool + tile, lane, off, vr);
   }
   if constexpr (kShared) {  // the shared prefix's partials, as more terms
@@ -610,7 +613,7 @@ __global__ __launch_bounds__(64) void decode_merge_append_pair_kernel(
     vrows.load(v_pool + tile, il);
 #pragma unroll
     for (int r = 0; r < NR; ++r)
-      k_pool[tile + (size_t)off * D + il + 32 * r] = kr[r];
+      __builtin_nontemporal_store(kr[r], k_pool + tile + (size_t)off * D + il + 32 * r);
     vrows.store(v_pool + tile, il, off, vr);
   }
 }
