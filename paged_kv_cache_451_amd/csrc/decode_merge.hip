@@ -494,6 +494,66 @@ __device__ inline void fold_range_partials_half(
   }
 }
 
+// The newest token's K row and V column for KV head g, written by all G
+// query heads of its group together (the two-heads-per-wave merge) when G
+// is a power of two and each head has at most one 16-byte chunk of the V
+// rows per lane: head n takes rows [n D/G, (n + 1) D/G), lane i the i-th
+// 16-byte chunk of those rows (both chunks of a row are rewritten, so the
+// head's stores cover whole cache lines) and K element n D/G + i.  The
+// chunk is read with the first round trip of loads and written back after
+// the partials are folded; only the loaded values are held through the
+// fold, the offsets are recomputed from (tile, n, G, i).
+template <int KB, int D, int kLanes>
+struct TokenShare {
+  typedef typename KvElem<KB>::raw RT;
+  static constexpr int kTokPerChunk = 16 / KB;  // tokens per 16-byte chunk
+  __device__ static bool usable(int G) {
+    return G >= 1 && (G & (G - 1)) == 0 && G <= D && (D / G) * KB <= kLanes;
+  }
+  u32x4 chunk;
+  RT v, k;
+  __device__ __forceinline__ static int chunk_at(int n, int G, int i) {
+    const int rph = D / G;  // rows per head
+    return (n * rph + i / KB) * kBlock + (i % KB) * kTokPerChunk;
+  }
+  __device__ __forceinline__ void load(const RT* __restrict__ v_pool,
+                                       const RT* __restrict__ k_new,
+                                       const RT* __restrict__ v_new,
+                                       size_t kv_row, size_t tile, int n,
+                                       int G, int i) {
+    const int rph = D / G;
+    const bool has_chunk = i < rph * KB;
+    chunk = has_chunk ? *reinterpret_cast<const u32x4*>(
+                            v_pool + tile + chunk_at(n, G, i))
+                      : u32x4{0, 0, 0, 0};
+    v = has_chunk ? v_new[kv_row + n * rph + i / KB] : RT(0);
+    k = i < rph ? k_new[kv_row + n * rph + i] : RT(0);
+  }
+  __device__ __forceinline__ void store(RT* __restrict__ k_pool,
+                                        RT* __restrict__ v_pool, size_t tile,
+                                        int off, int n, int G, int i) {
+    const int rph = D / G;
+    if (i < rph)
+      __builtin_nontemporal_store(k, k_pool + tile + (size_t)off * D +
+                                         n * rph + i);
+    if (i >= rph * KB) return;
+    if (i % KB == off / kTokPerChunk) {
+      constexpr int EPD = 4 / KB;  // elements per dword
+      const int within = off % kTokPerChunk;
+      const int dw = within / EPD;
+      const int shift = 8 * KB * (within % EPD);
+      const unsigned mask =
+          KB == 4 ? 0xFFFFFFFFu : (((1u << (8 * KB)) - 1u) << shift);
+      const unsigned val = ((unsigned)v << shift) & mask;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        chunk[e] = e == dw ? ((chunk[e] & ~mask) | val) : chunk[e];
+    }
+    __builtin_nontemporal_store(
+        chunk, reinterpret_cast<u32x4*>(v_pool + tile + chunk_at(n, G, i)));
+  }
+};
+
 // The same merge pass with one 64-lane workgroup per (sequence, pair of
 // query heads), for batches whose (sequence, query head) count exceeds the
 // waves the GPU holds at once: the first half of the wave takes head 2p,
@@ -561,12 +621,21 @@ __global__ __launch_bounds__(64) void decode_merge_append_pair_kernel(
     vr[r] = v_new[kv_row + d];
     qf[r] = (float)q[h_row * D + d];
   }
-  // the half of the group's first query head writes the token's slot, at
-  // the end (V as whole rows): reading the rows up front would hold 32 more
-  // registers through the fold, and this kernel must stay within 64 (8
-  // waves per SIMD, so that the grid runs in one round)
-  const bool writes = has_head && n == 0 && slot >= 0 &&
-                      slot < s.NB * kBlock;
+  // The token's slot: written by every head of the group together
+  // (TokenShare: one 16-byte chunk per lane, read with the loads above),
+  // else by the half of the group's first query head at the end (whole V
+  // rows: reading them up front would hold 32 more registers through the
+  // fold, and this kernel must stay within 64, 8 waves per SIMD, so that
+  // the grid runs in one round).
+  const bool slot_ok = has_head && slot >= 0 && slot < s.NB * kBlock;
+  const size_t tile =
+      slot_ok ? ((size_t)(slot >> 4) * s.Hkv + g) * kBlock * D : 0;
+  const int off = slot & (kBlock - 1);
+  typedef TokenShare<KB, D, 32> Share;
+  const bool shared_write = slot_ok && Share::usable(G);
+  Share share;
+  if (shared_write)
+    share.load(v_pool, k_new, v_new, kv_row, tile, n, G, il);
 
   float dot = 0.f;
 #pragma unroll
@@ -606,9 +675,9 @@ __global__ __launch_bounds__(64) void decode_merge_append_pair_kernel(
   OT* out = out_all + h_row * D;
 #pragma unroll
   for (int r = 0; r < NR; ++r) out[il + 32 * r] = (OT)(o[r] * inv);
-  if (writes) {
-    const size_t tile = ((size_t)(slot >> 4) * s.Hkv + g) * kBlock * D;
-    const int off = slot & (kBlock - 1);
+  if (shared_write) {
+    share.store(k_pool, v_pool, tile, off, n, G, il);
+  } else if (slot_ok && n == 0) {
     VRows<KB, D, 32> vrows;
     vrows.load(v_pool + tile, il);
 #pragma unroll
