@@ -77,7 +77,8 @@ def parse():
                         "quantisation); copy_blocks: copy-on-write of "
                         "--pairs whole blocks; engine: the synthetic "
                         "continuous-batching loop; prefill: chunked-prefill "
-                        "attention (--config prefill_llama3_8b_bf16); "
+                        "attention (--config prefill_llama3_8b_bf16, or "
+                        "prefill_llama3_8b_fp8 over an fp8 pool); "
                         "stream: the practical read ceiling (a plain "
                         "nontemporal read of --stream-mib MiB) at several "
                         "grid sizes")
@@ -494,7 +495,8 @@ def bench_prefill(a, torch, _lib):
            ("q", "k_pool", "v_pool", "block_tables", "seq_lens", "q_start")}
     out = torch.empty_like(dev["q"])
     desc = _lib.prefill_desc(dev["q"], dev["k_pool"], dev["block_tables"],
-                             cfg.num_seqs)
+                             cfg.num_seqs, k_scale=case.k_scale,
+                             v_scale=case.v_scale)
 
     def call():
         _lib.pa_prefill(dev["q"], dev["k_pool"], dev["v_pool"],
@@ -552,7 +554,8 @@ def bench_prefill(a, torch, _lib):
         "wall_ms_per_step": round(wall * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": name, "num_seqs": cfg.num_seqs,
+        "config": {"workload": name, "kv_dtype": cfg.kv_dtype,
+                   "num_seqs": cfg.num_seqs,
                    "chunk": cfg.chunk, "prior_tokens": [cfg.prior_lo,
                                                         cfg.prior_hi],
                    "num_q_heads": cfg.num_q_heads,

@@ -276,8 +276,8 @@ size_t pa_decode_append_shared_workspace_size(const pa_decode_desc* desc);
  *   workspace            at least
  *                        pa_decode_append_shared_workspace_size(desc)
  *                        bytes, 256-byte aligned.
- * Other arguments as for pa_decode_append; only bf16 q and bf16 pools,
- * head_size 64 or 128, and scale > 0 are supported.  total_blocks_hint, if
+ * Other arguments as for pa_decode_append; only bf16 q with bf16 or fp8
+ * e4m3fn pools, head_size 64 or 128, and scale > 0 are supported.  total_blocks_hint, if
  * given, should count the suffix blocks.  The caller guarantees that the
  * members' first P_j entries are equal; if they are not, the prefix of the
  * first member is used for all (memory-safe, numerically the first
@@ -394,7 +394,9 @@ int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_blocks,
  *   num_blocks          NB >= 1
  *   max_blocks_per_seq  row length of block_tables
  *   num_query_tokens    T = q_start[B], the packed query rows of q / out
- *   q_dtype, kv_dtype   both PA_BF16
+ *   q_dtype, kv_dtype   (BF16, BF16) or (BF16, FP8_E4M3FN)
+ *   k_scale, v_scale    per-tensor dequantisation scales of an FP8 pool
+ *                       (finite, > 0); ignored for BF16 pools.
  */
 typedef struct {
   int32_t num_seqs;
@@ -407,6 +409,8 @@ typedef struct {
   int32_t num_query_tokens;
   pa_dtype q_dtype;
   pa_dtype kv_dtype;
+  float k_scale;
+  float v_scale;
 } pa_prefill_desc;
 
 /*
@@ -423,7 +427,8 @@ typedef struct {
  * The result equals dense causal attention over the contiguous context
  * ("PagedAttention：KV cache 即虚拟内存", section "直接答案").
  *   q, out          [T][Hq][D] bf16, 16-byte aligned
- *   k_pool, v_pool  as for pa_decode (bf16)
+ *   k_pool, v_pool  as for pa_decode: bf16, or fp8 e4m3fn codes whose
+ *                   values are code * k_scale (K) and code * v_scale (V)
  *   block_tables    int32 [B][max_blocks_per_seq]
  *   seq_lens        int32 [B], the chunk included
  *   q_start         int32 [B+1], non-decreasing, q_start[B] = T
@@ -433,7 +438,8 @@ typedef struct {
  * block ids outside [0, NB) contribute nothing.
  * scale must be finite and positive (the kernel takes each step's row
  * maximum on the unscaled scores).
- * Errors: PA_ERR_NULL, PA_ERR_SHAPE (also for scale <= 0), PA_ERR_DTYPE,
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (also for scale <= 0 and for FP8 scales
+ * that are not finite and positive), PA_ERR_DTYPE,
  * PA_ERR_ALIGN, PA_ERR_LAUNCH.  Asynchronous on `stream`; no workspace.
  */
 int pa_prefill(const void* q, const void* k_pool, const void* v_pool,

@@ -57,4 +57,6 @@ def prefill_args(case, seqs=None):
                 block_tables=case.block_tables.numpy(),
                 seq_lens=case.seq_lens.numpy(),
                 q_start=case.q_start.numpy(), scale=case.scale,
-                q_dtype=q_dtype, kv_dtype=kv_dtype, seqs=seqs)
+                q_dtype=q_dtype, kv_dtype=kv_dtype,
+                k_scale=getattr(case, "k_scale", 1.0),
+                v_scale=getattr(case, "v_scale", 1.0), seqs=seqs)

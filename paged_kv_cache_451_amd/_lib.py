@@ -86,6 +86,8 @@ class PrefillDesc(ctypes.Structure):
         ("num_query_tokens", ctypes.c_int32),
         ("q_dtype", ctypes.c_int),
         ("kv_dtype", ctypes.c_int),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -349,6 +351,7 @@ def pa_decode_append_noalloc(q, k_pool, v_pool, block_tables, seq_lens,
 def pa_decode_append_shared(q, k_pool, v_pool, block_tables, seq_lens, scale,
                             out, k_new, v_new, slot_mapping, group_start,
                             group_prefix_blocks, *, max_seq_len: int,
+                            k_scale: float = 1.0, v_scale: float = 1.0,
                             total_blocks_hint: int = 0, num_waves: int = 0,
                             workspace: Optional[torch.Tensor] = None,
                             events: Optional[Sequence] = None,
@@ -367,6 +370,7 @@ def pa_decode_append_shared(q, k_pool, v_pool, block_tables, seq_lens, scale,
     lib = load()
     if desc is None:
         desc = decode_desc(q, k_pool, block_tables, max_seq_len=max_seq_len,
+                           k_scale=k_scale, v_scale=v_scale,
                            total_blocks_hint=total_blocks_hint,
                            num_waves=num_waves, events=events)
     if workspace is None:
@@ -433,18 +437,21 @@ def pa_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks) -> None:
                               _stream()))
 
 
-def prefill_desc(q, k_pool, block_tables, num_seqs: int) -> PrefillDesc:
+def prefill_desc(q, k_pool, block_tables, num_seqs: int, *,
+                 k_scale: float = 1.0, v_scale: float = 1.0) -> PrefillDesc:
     t, hq, d = q.shape
     nb, hkv, bs, _ = k_pool.shape
     return PrefillDesc(num_seqs=num_seqs, num_q_heads=hq, num_kv_heads=hkv,
                        head_size=d, block_size=bs, num_blocks=nb,
                        max_blocks_per_seq=block_tables.shape[1],
                        num_query_tokens=t, q_dtype=_DTYPE[q.dtype],
-                       kv_dtype=_DTYPE[k_pool.dtype])
+                       kv_dtype=_DTYPE[k_pool.dtype], k_scale=k_scale,
+                       v_scale=v_scale)
 
 
 def pa_prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, scale,
-               out, desc: Optional[PrefillDesc] = None) -> torch.Tensor:
+               out, desc: Optional[PrefillDesc] = None, *,
+               k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
     """Chunked-prefill attention into ``out`` (see ``include/pa.h``)."""
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must be [tokens, num_q_heads, head_size] "
@@ -456,7 +463,8 @@ def pa_prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, scale,
     _int32("q_start", q_start, b + 1)
     lib = load()
     if desc is None:
-        desc = prefill_desc(q, k_pool, block_tables, seq_lens.numel())
+        desc = prefill_desc(q, k_pool, block_tables, seq_lens.numel(),
+                            k_scale=k_scale, v_scale=v_scale)
     _check(lib.pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool),
                           _ptr(block_tables), _ptr(seq_lens), _ptr(q_start),
                           ctypes.c_float(scale), _ptr(out),

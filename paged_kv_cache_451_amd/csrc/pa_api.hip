@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 // Upper bound on 64-lane workgroups per compute unit the schedule aims for;
 // the kernel's register budget may allow fewer.  Measured on MI355X: four
 // per CU streams as fast as eight or more while giving each range twice the
@@ -221,7 +221,8 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
   if (st != PA_OK) return st;
   const bool fused = k_new != nullptr;
   if (sp) {
-    if (desc->q_dtype != PA_BF16 || desc->kv_dtype != PA_BF16)
+    if (desc->q_dtype != PA_BF16 ||
+        (desc->kv_dtype != PA_BF16 && desc->kv_dtype != PA_FP8_E4M3FN))
       return PA_ERR_DTYPE;
     if ((desc->head_size != 64 && desc->head_size != 128) ||
         sp->num_groups < 0 || sp->num_groups > desc->num_seqs)
@@ -326,8 +327,10 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
     pf.s.NB = desc->num_blocks;
     pf.s.T = desc->num_seqs;
     pf.s.c_log2 = a.s.c_log2;
+    pf.s.v_scale = a.s.v_scale;
     pf.s.splits = p.splits;
-    const hipError_t e = pa::launch_shared_prefix(desc->head_size, pf, s);
+    const hipError_t e = pa::launch_shared_prefix(
+        desc->head_size, desc->kv_dtype == PA_FP8_E4M3FN, pf, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
 
     a.block_tables = st_tab;
@@ -591,7 +594,13 @@ int pa_prefill(const void* q, const void* k_pool, const void* v_pool,
       d->max_blocks_per_seq < 1 ||
       (int64_t)d->max_blocks_per_seq * pa::kBlock > INT32_MAX)
     return PA_ERR_SHAPE;
-  if (d->q_dtype != PA_BF16 || d->kv_dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (d->q_dtype != PA_BF16 ||
+      (d->kv_dtype != PA_BF16 && d->kv_dtype != PA_FP8_E4M3FN))
+    return PA_ERR_DTYPE;
+  const bool fp8 = d->kv_dtype == PA_FP8_E4M3FN;
+  if (fp8 && !(d->k_scale > 0.f && d->v_scale > 0.f && isfinite(d->k_scale) &&
+               isfinite(d->v_scale)))
+    return PA_ERR_SHAPE;
   const int G = d->num_q_heads / d->num_kv_heads;
   if ((int64_t)d->num_query_tokens * d->num_q_heads > INT32_MAX ||
       pa::prefill_grid(d->head_size, d->num_query_tokens, G, d->num_seqs,
@@ -621,7 +630,9 @@ int pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   a.s.max_blocks = d->max_blocks_per_seq;
   a.s.NB = d->num_blocks;
   a.s.T = d->num_query_tokens;
-  a.s.c_log2 = (float)((double)scale * 1.4426950408889634);
+  a.s.c_log2 = (float)((double)scale * 1.4426950408889634 *
+                       (fp8 ? (double)d->k_scale : 1.0));
+  a.s.v_scale = fp8 ? d->v_scale : 1.f;
   a.s.splits = 1;
   a.s.attn_grid = 0;
   a.member_lens = nullptr;
@@ -630,7 +641,7 @@ int pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   a.part_ml = nullptr;
   a.part_o = nullptr;
   hipError_t e =
-      pa::launch_prefill(d->head_size, a, static_cast<hipStream_t>(stream));
+      pa::launch_prefill(d->head_size, fp8, a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -103,7 +103,8 @@ struct PrefillSched {
   int max_blocks;  // row length of block_tables
   int NB;          // pool blocks
   int T;           // packed query rows (q_start[B])
-  float c_log2;    // scale * log2(e)
+  float c_log2;    // scale * log2(e) * k_scale
+  float v_scale;   // fp8 pools: V dequantisation scale (else 1)
   int splits;      // shared-prefix pass: key ranges per group (else 1)
   int attn_grid;   // workgroups of the attention part (set by the launcher)
 };
@@ -125,7 +126,8 @@ struct PrefillArgs {
 };
 // Workgroups the prefill launch uses (an upper bound on the query tiles).
 int64_t prefill_grid(int head_size, int64_t T, int G, int B, int Hkv);
-hipError_t launch_prefill(int head_size, const PrefillArgs& a,
+// kv_fp8: the pools hold fp8 e4m3fn codes (else bf16).
+hipError_t launch_prefill(int head_size, bool kv_fp8, const PrefillArgs& a,
                           hipStream_t stream);
 // Shared-prefix pass of cascade decode (same kernel, s.B = groups, s.T =
 // decode sequences), s.splits key ranges per group: partials
@@ -134,8 +136,8 @@ hipError_t launch_prefill(int head_size, const PrefillArgs& a,
 // P_b] (-1 past the row), suffix_lens[b] = max(0, L_b - 16 P_b), where P_b
 // is the prefix blocks of b's group (0 outside every group); sequences
 // outside every group get empty partials (m = -inf, l = 0).
-hipError_t launch_shared_prefix(int head_size, const PrefillArgs& a,
-                                hipStream_t stream);
+hipError_t launch_shared_prefix(int head_size, bool kv_fp8,
+                                const PrefillArgs& a, hipStream_t stream);
 
 // Copy-on-write block copy: K and V block src[i] -> dst[i] for every pair
 // (block_bytes per pool block, a multiple of 16).  Pairs with an id outside

@@ -32,7 +32,11 @@
 // others (K two steps ahead, V one step ahead).  The copies go from
 // the pool straight into LDS (no registers on the way), wave w copying
 // block w of the step; unpadded rows with XOR-swizzled 16-byte chunks keep
-// the operand reads free of bank conflicts.  Keys at or past the sequence
+// the operand reads free of bank conflicts.  An fp8 e4m3fn pool takes a
+// different road into the same LDS layout: each lane loads 16-byte pieces
+// of its wave's tiles into registers, widens them exactly to bf16 and
+// writes them to LDS before the step's barrier (k_scale is folded into the
+// score scale, v_scale into the output).  Keys at or past the sequence
 // end, or in blocks with an out-of-range id, get a -inf score, and their V
 // is zeroed in LDS after the copy lands (a masked probability times them
 // must be 0 even where the slot holds NaN).  The causal mask is applied only
@@ -359,10 +363,10 @@ __device__ void suffix_row(int b, const int32_t* __restrict__ tables,
   }
 }
 
-template <int D, bool kShared>
+template <int D, bool kShared, bool kFP8>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k_pool,
-    const __bf16* __restrict__ v_pool,
+    const __bf16* __restrict__ q, const void* __restrict__ k_pool,
+    const void* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ q_start, __bf16* __restrict__ out,
@@ -497,7 +501,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   constexpr int RPI = kWave / CPR;       // K rows per instruction
   constexpr int IPT = kBlock / RPI;      // instructions per tile
   static_assert(kPfWaves == 4 && IPT * 1024 == kBlock * D * 2, "copy geometry");
-  const size_t tile_bytes = (size_t)kBlock * D * 2;
+  const size_t tile_bytes = (size_t)kBlock * D * (kFP8 ? 1 : 2);
   const char* kp = reinterpret_cast<const char*>(k_pool) + (size_t)g * tile_bytes;
   const char* vp = reinterpret_cast<const char*>(v_pool) + (size_t)g * tile_bytes;
   const size_t blk_stride = (size_t)sc.Hkv * tile_bytes;
@@ -545,6 +549,61 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     tile_copy(vp, ids_raw,
               lds + Lay::V0 + buf * Lay::VBytes + wave * Lay::VTile, v_src);
   };
+  // fp8 pools: lane l loads bytes 1024 m + 16 l (m < IPF) of its wave's K
+  // tile and of its V tile into registers: 16 d values of one key, or the
+  // 16 tokens of one d row.  Widened to bf16 they are two 16-byte chunks of
+  // the bf16 layout above: kf_dst / vf_dst hold the LDS offset of the
+  // first, the second sits at that offset ^ 16 (the chunks' positions
+  // differ in their lowest bit).
+  constexpr int IPF = kBlock * D / 1024;
+  uint32_t kf_dst[IPF], vf_dst[IPF];
+#pragma unroll
+  for (int m = 0; m < IPF; ++m) {
+    const int byte = 1024 * m + 16 * lane;
+    const int tok = byte / D, u = (byte % D) / 16;
+    const int kr = kBlock * wave + k_lds_row(tok);
+    kf_dst[m] = (uint32_t)(kr * Lay::KRow + ((2 * u) ^ kswz<D>(kr)) * 16);
+    const int d = byte / 16;
+    vf_dst[m] = (uint32_t)(d * 32 + ((d >> 3) & 1) * 16);
+  }
+  typedef u32x4 Raw8[IPF];
+#if defined(__HIP_DEVICE_COMPILE__)
+  auto load_tile8 = [&](const char* pool, int ids_raw, Raw8& raw) {
+    const int r = readlane(ids_raw, wave);
+    const int id = (unsigned)r < (unsigned)sc.NB ? r : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(pool + (size_t)id * blk_stride), 0, (int)tile_bytes,
+        kBufferWord3);
+#pragma unroll
+    for (int m = 0; m < IPF; ++m)
+      raw[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, 1024 * m + 16 * lane,
+                                                     0, 0);
+  };
+#else
+  auto load_tile8 = [](const char*, int, Raw8&) {};
+#endif
+  // 16 fp8 e4m3fn codes -> 16 bf16 (exact), stored as two LDS chunks
+  auto widen_store = [&](const Raw8& raw, uint8_t* base,
+                         const uint32_t (&dst)[IPF]) {
+#pragma unroll
+    for (int m = 0; m < IPF; ++m) {
+      unsigned w[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[m][k], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[m][k], true);
+        w[2 * k] = __builtin_bit_cast(unsigned,
+                                      __builtin_convertvector(lo, bf16x2));
+        w[2 * k + 1] = __builtin_bit_cast(unsigned,
+                                          __builtin_convertvector(hi, bf16x2));
+      }
+      *reinterpret_cast<u32x4*>(base + dst[m]) = u32x4{w[0], w[1], w[2], w[3]};
+      *reinterpret_cast<u32x4*>(base + (dst[m] ^ 16u)) =
+          u32x4{w[4], w[5], w[6], w[7]};
+    }
+  };
+  uint8_t* const v_wave = lds + Lay::V0 + wave * Lay::VTile;
+
   // Zeroes V of tokens at or past nvs[u] in the V tiles of buffer buf (a
   // masked probability times them must be 0, also where the slot holds NaN).
   auto zero_v_tail = [&](int buf, const int nvs[4]) {
@@ -687,13 +746,25 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   if (s_end > s_begin) {
     const int e0 = table_entry(s_begin);
     e1 = table_entry(last < s_begin + 1 ? last : s_begin + 1);
-    issue_k(0, e0);
-    issue_v(0, e0);
-    if (last > s_begin) issue_k(1, e1);
+    Raw8 k0, v0, k1;
+    if constexpr (kFP8) {
+      load_tile8(kp, e0, k0);
+      load_tile8(vp, e0, v0);
+      if (last > s_begin) load_tile8(kp, e1, k1);
+    } else {
+      issue_k(0, e0);
+      issue_v(0, e0);
+      if (last > s_begin) issue_k(1, e1);
+    }
     int nv0[4];
     valid_of(s_begin, e0, nv0);
     e2 = table_entry(last < s_begin + 2 ? last : s_begin + 2);
     wait_all_memory();
+    if constexpr (kFP8) {
+      widen_store(k0, lds, kf_dst);
+      widen_store(v0, v_wave, vf_dst);
+      if (last > s_begin) widen_store(k1, lds + Lay::KBytes, kf_dst);
+    }
     __syncthreads();
     if (partial(nv0)) {
       zero_v_tail(0, nv0);
@@ -738,9 +809,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     // the table entries of step s + 3 are loaded before this step's copies
     // are issued, so that waiting for them leaves the copies in flight
     const int e3 = table_entry(s + 3 < last ? s + 3 : last);
+    Raw8 kraw, vraw;  // fp8 pools: the copies, held until the step's end
     if (kMore) {
-      if (s + 2 <= last) issue_k(cb, e2);
-      issue_v(nb, e1);
+      if constexpr (kFP8) {
+        if (s + 2 <= last) load_tile8(kp, e2, kraw);
+        load_tile8(vp, e1, vraw);
+      } else {
+        if (s + 2 <= last) issue_k(cb, e2);
+        issue_v(nb, e1);
+      }
       valid_of(s + 1, e1, nv_nxt);
     }
 
@@ -808,6 +885,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
       m_cand = max_xor32(mx) * sc.c_log2;
 
       wait_all_memory();
+      if constexpr (kFP8) {
+        if (s + 2 <= last) widen_store(kraw, lds + cb * Lay::KBytes, kf_dst);
+        widen_store(vraw, v_wave + nb * Lay::VBytes, vf_dst);
+      }
       __syncthreads();
       if (partial(nv_nxt)) {
         zero_v_tail(nb, nv_nxt);
@@ -842,19 +923,20 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
         part_ml[hrow * 2 + 1] = ltot;
       }
       float* orow = part_o + hrow * D + 4 * h;
+      const float vs = kFP8 ? sc.v_scale : 1.f;
 #pragma unroll
       for (int X = 0; X < NX; ++X)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const float4 o = {acc[X][4 * a], acc[X][4 * a + 1],
-                            acc[X][4 * a + 2], acc[X][4 * a + 3]};
+          const float4 o = {acc[X][4 * a] * vs, acc[X][4 * a + 1] * vs,
+                            acc[X][4 * a + 2] * vs, acc[X][4 * a + 3] * vs};
           *reinterpret_cast<float4*>(orow + 32 * X + 8 * a) = o;
         }
     }
     return;
   }
   if (row_ok) {
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float inv = ltot > 0.f ? (kFP8 ? sc.v_scale : 1.f) / ltot : 0.f;
     __bf16* orow =
         out + ((size_t)(qs + ti) * sc.Hq + (size_t)g * G + hn) * D + 4 * h;
 #pragma unroll
@@ -869,7 +951,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   }
 }
 
-template <int D, bool kShared>
+template <int D, bool kShared, bool kFP8>
 void launch_pf(const PrefillArgs& a, hipStream_t stream) {
   const int tiles =
       (int)(((int64_t)a.s.T * a.s.G + kCols - 1) / kCols) + a.s.B;
@@ -877,14 +959,27 @@ void launch_pf(const PrefillArgs& a, hipStream_t stream) {
   PrefillSched s = a.s;
   s.attn_grid = tiles * a.s.Hkv * splits;
   const int grid = s.attn_grid + (kShared ? a.s.T : 0);
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, kShared>), dim3((unsigned)grid),
-                     dim3(kPfThreads), 0,
-                     stream, reinterpret_cast<const __bf16*>(a.q),
-                     reinterpret_cast<const __bf16*>(a.k_pool),
-                     reinterpret_cast<const __bf16*>(a.v_pool), a.block_tables,
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, kShared, kFP8>),
+                     dim3((unsigned)grid), dim3(kPfThreads), 0, stream,
+                     reinterpret_cast<const __bf16*>(a.q), a.k_pool, a.v_pool,
+                     a.block_tables,
                      a.seq_lens, a.q_start, reinterpret_cast<__bf16*>(a.out),
                      a.member_lens, a.part_ml, a.part_o, a.suffix_tables,
                      a.suffix_lens, s);
+}
+
+template <bool kShared>
+hipError_t launch_pf_any(int head_size, bool kv_fp8, const PrefillArgs& a,
+                         hipStream_t stream) {
+  if (a.s.B == 0 || a.s.T == 0) return hipSuccess;
+  switch (head_size * 2 + (kv_fp8 ? 1 : 0)) {
+    case 128: launch_pf<64, kShared, false>(a, stream); break;
+    case 129: launch_pf<64, kShared, true>(a, stream); break;
+    case 256: launch_pf<128, kShared, false>(a, stream); break;
+    case 257: launch_pf<128, kShared, true>(a, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -894,26 +989,14 @@ int64_t prefill_grid(int head_size, int64_t T, int G, int B, int Hkv) {
   return ((T * G + kCols - 1) / kCols + B) * Hkv;
 }
 
-hipError_t launch_prefill(int head_size, const PrefillArgs& a,
+hipError_t launch_prefill(int head_size, bool kv_fp8, const PrefillArgs& a,
                           hipStream_t stream) {
-  if (a.s.B == 0 || a.s.T == 0) return hipSuccess;
-  switch (head_size) {
-    case 64: launch_pf<64, false>(a, stream); break;
-    case 128: launch_pf<128, false>(a, stream); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return launch_pf_any<false>(head_size, kv_fp8, a, stream);
 }
 
-hipError_t launch_shared_prefix(int head_size, const PrefillArgs& a,
-                                hipStream_t stream) {
-  if (a.s.B == 0 || a.s.T == 0) return hipSuccess;
-  switch (head_size) {
-    case 64: launch_pf<64, true>(a, stream); break;
-    case 128: launch_pf<128, true>(a, stream); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+hipError_t launch_shared_prefix(int head_size, bool kv_fp8,
+                                const PrefillArgs& a, hipStream_t stream) {
+  return launch_pf_any<true>(head_size, kv_fp8, a, stream);
 }
 
 }  // namespace pa

@@ -365,6 +365,7 @@ class PrefillConfig:
     prior_lo: int                  # cached tokens before the chunk:
     prior_hi: int                  #   uniform[prior_lo, prior_hi]
     description: str = ""
+    kv_dtype: str = "bf16"         # or "fp8_e4m3fn" (per-tensor scales)
 
     @property
     def group(self) -> int:
@@ -380,6 +381,11 @@ PREFILL_CONFIGS: List[PrefillConfig] = [
         prior_hi=3584,
         description="8 seqs, a 512-token chunk each after uniform[0,3584] "
                     "cached tokens, 32 q / 8 KV heads, D=128, bf16"),
+    PrefillConfig(
+        "prefill_llama3_8b_fp8", 8, 32, 8, 128, chunk=512, prior_lo=0,
+        prior_hi=3584, kv_dtype="fp8_e4m3fn",
+        description="the same chunks over an fp8 e4m3fn K/V pool "
+                    "(per-tensor scales amax/448), bf16 q and output"),
 ]
 PREFILL_BY_NAME = {c.name: c for c in PREFILL_CONFIGS}
 
@@ -395,6 +401,8 @@ class PrefillCase:
     block_tables: torch.Tensor
     seq_lens: torch.Tensor        # cached tokens including the chunk
     scale: float
+    k_scale: float = 1.0          # fp8 pools: stored code * scale = value
+    v_scale: float = 1.0
 
     @property
     def num_tokens(self) -> int:
@@ -425,8 +433,12 @@ def build_prefill_case(cfg: PrefillConfig, seed: int = 0,
     q32 = _normal_f32(kids[2], (int(q_start[-1]), cfg.num_q_heads, d))
     k32 = _normal_f32(kids[3], (nb, hkv, BLOCK_SIZE, d))
     v32 = _normal_f32(kids[4], (nb, hkv, d, BLOCK_SIZE))
-    k_pool = _to_storage(k32, "bf16")
-    v_pool = _to_storage(v32, "bf16")
+    k_scale = v_scale = 1.0
+    if cfg.kv_dtype == "fp8_e4m3fn":
+        k_scale = float(np.float32(np.abs(k32).max() / FP8_MAX))
+        v_scale = float(np.float32(np.abs(v32).max() / FP8_MAX))
+    k_pool = _to_storage(k32, cfg.kv_dtype, k_scale)
+    v_pool = _to_storage(v32, cfg.kv_dtype, v_scale)
     # slots past each sequence's length (and free blocks) hold NaN
     written = np.zeros((nb, BLOCK_SIZE), dtype=bool)
     for i in range(b):
@@ -437,15 +449,20 @@ def build_prefill_case(cfg: PrefillConfig, seed: int = 0,
             written[tables[i, nfull], :rem] = True
     blk_idx, tok_idx = torch.nonzero(torch.from_numpy(~written),
                                      as_tuple=True)
-    nan = _nan_of("bf16")
-    k_pool[blk_idx, :, tok_idx, :] = nan
-    v_pool[blk_idx, :, :, tok_idx] = nan
+    nan = _nan_of(cfg.kv_dtype)
+    if cfg.kv_dtype == "fp8_e4m3fn":  # index_put on the raw bytes
+        k_pool.view(torch.uint8)[blk_idx, :, tok_idx, :] = nan.view(torch.uint8)
+        v_pool.view(torch.uint8)[blk_idx, :, :, tok_idx] = nan.view(torch.uint8)
+    else:
+        k_pool[blk_idx, :, tok_idx, :] = nan
+        v_pool[blk_idx, :, :, tok_idx] = nan
     return PrefillCase(
         config=cfg, seed=seed, q=_to_storage(q32, "bf16"),
         q_start=torch.from_numpy(q_start), k_pool=k_pool, v_pool=v_pool,
         block_tables=torch.from_numpy(tables),
         seq_lens=torch.from_numpy(seq_lens.astype(np.int32)),
-        scale=float(np.float32(1.0 / math.sqrt(d))))
+        scale=float(np.float32(1.0 / math.sqrt(d))), k_scale=k_scale,
+        v_scale=v_scale)
 
 
 # --------------------------------------------------------------------------

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
     assert lib.pa_status_string(0) == b"success"
     for st in range(-8, 0):
         assert lib.pa_status_string(st) not in (b"", b"unknown status")
@@ -140,7 +140,12 @@ def test_shared_prefix_step_checks(lib):
         return f(p, p, p, p, p, ctypes.c_float(scale), p, kn, p, p, gs, gp,
                  ng, ctypes.byref(desc), p, 1 << 20, None)
 
-    assert call(_desc(kv_dtype=_lib.PA_FP8_E4M3FN)) == -2
+    # fp8 pools pass the dtype check and are held to the fp8 scale check
+    assert call(_desc(kv_dtype=_lib.PA_FP8_E4M3FN, k_scale=0.0)) == -3
+    assert call(_desc(kv_dtype=_lib.PA_FP8_E4M3FN,
+                      v_scale=float("inf"))) == -3
+    assert call(_desc(q_dtype=_lib.PA_F32,
+                      kv_dtype=_lib.PA_FP8_E4M3FN)) == -2
     assert call(_desc(q_dtype=_lib.PA_F32, kv_dtype=_lib.PA_F32,
                       num_q_heads=4)) == -2
     assert call(_desc(head_size=256)) == -3
@@ -237,8 +242,14 @@ def test_prefill_checks(lib):
     one = ctypes.c_float(1.0)
     for bad, st in [(dict(head_size=256), -3), (dict(num_q_heads=2 * 17), -3),
                     (dict(num_q_heads=7), -3), (dict(block_size=8), -3),
-                    (dict(kv_dtype=_lib.PA_FP8_E4M3FN), -2),
+                    (dict(kv_dtype=_lib.PA_F32), -2),
                     (dict(q_dtype=_lib.PA_F32), -2),
+                    (dict(q_dtype=_lib.PA_F32,
+                          kv_dtype=_lib.PA_FP8_E4M3FN), -2),
+                    # fp8 pools need finite positive scales
+                    (dict(kv_dtype=_lib.PA_FP8_E4M3FN), -3),
+                    (dict(kv_dtype=_lib.PA_FP8_E4M3FN, k_scale=1.0,
+                          v_scale=float("nan")), -3),
                     (dict(num_query_tokens=-1), -3)]:
         d = desc(**bad)
         assert f(p, p, p, p, p, p, one, p, ctypes.byref(d), None) == st, bad

@@ -20,11 +20,12 @@ from conftest import appended_pools, oracle_args, raw_bits
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
+TOL_FP8 = 6e-2  # fp8 e4m3fn pools, as for every fp8 decode step
 
 
-def small_prefix_case(seed=0):
+def small_prefix_case(seed=0, kv_dtype="bf16"):
     cfg = CONFIG_BY_NAME["prefix_shared_bf16"].replace(
-        num_seqs=8, prefix_len=512, lo=1, hi=300)
+        num_seqs=8, prefix_len=512, lo=1, hi=300, kv_dtype=kv_dtype)
     return build_case(cfg, seed)
 
 
@@ -50,6 +51,7 @@ def run_shared(case, groups, prefix_blocks, dev=None, tables=None,
         dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
         dev["seq_lens"], case.scale, out, dev["k_new"], dev["v_new"],
         dev["slot_mapping"], gs, gp, max_seq_len=case.max_seq_len,
+        k_scale=case.k_scale, v_scale=case.v_scale,
         total_blocks_hint=total_blocks_hint)
     torch.cuda.synchronize()
     return out, dev
@@ -62,7 +64,8 @@ def run_plain(case, dev=None, tables=None):
     _lib.pa_decode_append(
         dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
         dev["seq_lens"], case.scale, out, dev["k_new"], dev["v_new"],
-        dev["slot_mapping"], max_seq_len=case.max_seq_len)
+        dev["slot_mapping"], max_seq_len=case.max_seq_len,
+        k_scale=case.k_scale, v_scale=case.v_scale)
     torch.cuda.synchronize()
     return out, dev
 
@@ -113,8 +116,21 @@ def test_shared_prompt_full_size():
     assert_pools_appended(case, dev)
 
 
-def test_no_group_and_empty_prefix_give_the_plain_step_bits():
-    case = small_prefix_case(seed=1)
+def test_shared_prompt_fp8_pool_matches_oracle():
+    """fp8 e4m3fn pools: the shared-prefix pass widens the prefix tiles to
+    bf16 in LDS and scales its partials by v_scale, the suffix and merge
+    passes are the fp8 decode step's."""
+    case = small_prefix_case(seed=2, kv_dtype="fp8_e4m3fn")
+    assert case.k_pool.dtype == torch.float8_e4m3fn
+    p = case.config.prefix_len // 16
+    out, dev = run_shared(case, [0, 3, case.config.num_seqs], [p, p - 5])
+    assert max_err(out, oracle_ref(case)) <= TOL_FP8
+    assert_pools_appended(case, dev)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_no_group_and_empty_prefix_give_the_plain_step_bits(kv_dtype):
+    case = small_prefix_case(seed=1, kv_dtype=kv_dtype)
     ref, _ = run_plain(case)
     for groups, pb in [(None, None), ([0, 8], [0]), ([0, 3, 8], [0, 0])]:
         out, _ = run_shared(case, groups, pb)

@@ -2,7 +2,10 @@
 
 Tolerance: max absolute error 2e-2 against the float64 oracle (bf16 q, K,
 V and output; the kernel rounds probabilities to bf16 before the PV
-product, as the decode kernel does).  Reduced cases span many 64-key steps,
+product, as the decode kernel does).  The fp8 e4m3fn pools are held to the
+same bound: their codes widen exactly to bf16 and the oracle reads the same
+codes times the same scales, so only the arithmetic's rounding differs
+(tighter than the 6e-2 allowed for fp8 KV in decode).  Reduced cases span many 64-key steps,
 several query tiles per sequence, ragged chunks and ragged last blocks; the
 full-size case runs the benchmark's configuration and compares every output
 element.
@@ -21,6 +24,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
 FULL = "prefill_llama3_8b_bf16"
+FULL_FP8 = "prefill_llama3_8b_fp8"
 
 
 def cfg(**kw):
@@ -35,7 +39,8 @@ def run(case, **over):
     out = torch.full_like(dev["q"], float("nan"))
     _lib.pa_prefill(dev["q"], dev["k_pool"], dev["v_pool"],
                     dev["block_tables"], dev["seq_lens"], dev["q_start"],
-                    case.scale, out)
+                    case.scale, out, k_scale=case.k_scale,
+                    v_scale=case.v_scale)
     torch.cuda.synchronize()
     return out.cpu()
 
@@ -91,22 +96,44 @@ def test_prefill_matches_oracle_small(gpu_lib, name, over, chunks):
     assert max_err(out, ref) <= TOL
 
 
-def test_prefill_full_size(gpu_lib):
-    """The benchmark's prefill workload in its launch configuration: every
-    (query token, head, column) against the oracle."""
-    case = build_prefill_case(PREFILL_BY_NAME[FULL], seed=0)
+# fp8 e4m3fn pools: the register-staged copies that widen each tile into
+# the bf16 LDS layout, at both head sizes, over ragged chunks and blocks,
+# odd and even step counts and the general tile search
+FP8 = [(name, dict(over, kv_dtype="fp8_e4m3fn"), chunks)
+       for name, over, chunks in SMALL
+       if name in ("llama_g4", "ragged", "g1_d64", "g16_d64", "step_edges",
+                   "step_edges_d64", "many_seqs")]
+
+
+@pytest.mark.parametrize("name, over, chunks", FP8,
+                         ids=[s[0] + "_fp8" for s in FP8])
+def test_prefill_fp8_pool_matches_oracle_small(gpu_lib, name, over, chunks):
+    case = build_prefill_case(cfg(**over), seed=5, chunks=chunks)
+    assert case.k_pool.dtype == torch.float8_e4m3fn
+    out = run(case)
+    ref = oracle.paged_prefill(**prefill_args(case))
+    assert max_err(out, ref) <= TOL
+
+
+@pytest.mark.parametrize("name", [FULL, FULL_FP8])
+def test_prefill_full_size(gpu_lib, name):
+    """The benchmark's prefill workloads in their launch configuration:
+    every (query token, head, column) against the oracle."""
+    case = build_prefill_case(PREFILL_BY_NAME[name], seed=0)
     out = run(case)
     ref = oracle.paged_prefill(**prefill_args(case))
     err = max_err(out, ref)
-    print(f"prefill full size, all {case.num_tokens} query tokens: max abs "
+    print(f"{name} full size, all {case.num_tokens} query tokens: max abs "
           f"err {err:.3e}")
     assert err <= TOL
 
 
-def test_one_token_chunks_equal_decode(gpu_lib):
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_one_token_chunks_equal_decode(gpu_lib, kv_dtype):
     """A chunk of one token is a decode step: same result as pa_decode."""
     from paged_kv_cache_451_amd import _lib
-    case = build_prefill_case(cfg(num_seqs=5, prior_lo=0, prior_hi=900),
+    case = build_prefill_case(cfg(num_seqs=5, prior_lo=0, prior_hi=900,
+                                  kv_dtype=kv_dtype),
                               seed=7, chunks=[1] * 5)
     out = run(case)
     dev = {k: getattr(case, k).cuda() for k in
@@ -114,7 +141,8 @@ def test_one_token_chunks_equal_decode(gpu_lib):
     dec = torch.empty_like(dev["q"])
     _lib.pa_decode(dev["q"], dev["k_pool"], dev["v_pool"],
                    dev["block_tables"], dev["seq_lens"], case.scale, dec,
-                   max_seq_len=int(case.seq_lens.max()))
+                   max_seq_len=int(case.seq_lens.max()),
+                   k_scale=case.k_scale, v_scale=case.v_scale)
     torch.cuda.synchronize()
     d = dec.cpu().to(torch.float64).numpy()
     assert np.abs(out.to(torch.float64).numpy() - d).max() <= TOL
@@ -122,14 +150,17 @@ def test_one_token_chunks_equal_decode(gpu_lib):
     assert max_err(out, ref) <= TOL
 
 
-def test_block_permutation_is_bitwise_invariant(gpu_lib):
-    case = build_prefill_case(cfg(num_seqs=4, chunk=70, prior_hi=300),
-                              seed=11)
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_block_permutation_is_bitwise_invariant(gpu_lib, kv_dtype):
+    case = build_prefill_case(cfg(num_seqs=4, chunk=70, prior_hi=300,
+                                  kv_dtype=kv_dtype), seed=11)
     out = run(case)
     nb = case.k_pool.shape[0]
     pi = torch.from_numpy(np.random.default_rng(2).permutation(nb))
-    kp, vp = torch.empty_like(case.k_pool), torch.empty_like(case.v_pool)
-    kp[pi], vp[pi] = case.k_pool, case.v_pool
+    kb, vb = case.k_pool.view(torch.uint8), case.v_pool.view(torch.uint8)
+    kp, vp = torch.empty_like(kb), torch.empty_like(vb)
+    kp[pi], vp[pi] = kb, vb
+    kp, vp = kp.view(case.k_pool.dtype), vp.view(case.v_pool.dtype)
     tab = case.block_tables
     tab2 = torch.where(tab >= 0, pi[tab.clamp(min=0).long()].to(torch.int32),
                        tab)
@@ -185,9 +216,10 @@ def test_chunk_longer_than_sequence(gpu_lib):
     assert max_err(out[60:], ref1) <= TOL
 
 
-def test_out_of_range_block_ids_are_not_dereferenced(gpu_lib):
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_out_of_range_block_ids_are_not_dereferenced(gpu_lib, kv_dtype):
     case = build_prefill_case(cfg(num_seqs=4, chunk=40, prior_lo=60,
-                                  prior_hi=200), seed=19)
+                                  prior_hi=200, kv_dtype=kv_dtype), seed=19)
     tab = case.block_tables.clone()
     nb = case.k_pool.shape[0]
     tab[1, 0] = nb + 1000
