@@ -188,19 +188,21 @@ def test_out_of_range_group_values_are_contained():
     assert max_err(out, oracle_ref(case)) <= TOL
 
 
-@pytest.mark.parametrize("hq, hkv, d", [(32, 4, 128), (8, 8, 64),
-                                        (16, 2, 64)])
-def test_shared_prompts_other_head_shapes(hq, hkv, d):
-    """G = 8 and G = 1 at D = 128 and D = 64: two groups, one sequence
-    outside both."""
+@pytest.mark.parametrize("hq, hkv, d, kv_dtype", [
+    (32, 4, 128, "bf16"), (8, 8, 64, "bf16"), (16, 2, 64, "bf16"),
+    (16, 2, 64, "fp8_e4m3fn"), (32, 4, 128, "fp8_e4m3fn")])
+def test_shared_prompts_other_head_shapes(hq, hkv, d, kv_dtype):
+    """G = 8 and G = 1 at D = 128 and D = 64 (and fp8 pools at both head
+    sizes): two groups, one sequence outside both."""
     cfg = CONFIG_BY_NAME["llama3_8b_bf16"].replace(
         num_seqs=7, num_q_heads=hq, num_kv_heads=hkv, head_size=d, lo=300,
-        hi=900)
+        hi=900, kv_dtype=kv_dtype)
     case = build_case(cfg, 31)
     groups, pb = [0, 4, 6], [15, 9]  # sequence 6 outside every group
     tab = _grouped_tables(case, groups, pb)
     out, dev = run_shared(case, groups, pb, tables=tab)
-    assert max_err(out, oracle_ref(case, tables=tab)) <= TOL
+    tol = TOL_FP8 if kv_dtype == "fp8_e4m3fn" else TOL
+    assert max_err(out, oracle_ref(case, tables=tab)) <= tol
     assert_pools_appended(case, dev)
 
 
