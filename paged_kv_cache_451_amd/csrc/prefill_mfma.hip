@@ -1,4 +1,5 @@
-// Paged chunked-prefill attention on gfx950 matrix cores (bf16 q, bf16 KV).
+// Paged chunked-prefill attention on gfx950 matrix cores (bf16 q; bf16 or
+// fp8 e4m3fn KV).
 //
 // Sequence b holds L cached tokens, the last C of which are this chunk's;
 // query row (token i, head n) of the chunk attends to the keys at positions
@@ -697,7 +698,6 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
     mx = fmaxf(mx, sv[hf][e]);
     return fmaxf(mx, sv[hf][e + 1]);
   };
-  // Probabilities of element pair q into the P operand, and their sum.
   // Probabilities of element pair q into the P operand (one packed word of
   // two bf16), and their sum.
   auto exp_pair = [&](const f32x16 (&sv)[2], int q, float m_use,
