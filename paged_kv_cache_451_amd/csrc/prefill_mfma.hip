@@ -583,7 +583,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
 #else
   auto load_tile8 = [](const char*, int, Raw8&) {};
 #endif
-  // 16 fp8 e4m3fn codes -> 16 bf16 (exact), stored as two LDS chunks
+  // 16 fp8 e4m3fn codes -> 16 bf16 (exact: every e4m3fn value is a bf16
+  // value, written directly by the scaled conversion with scale 1), stored
+  // as two LDS chunks
   auto widen_store = [&](const Raw8& raw, uint8_t* base,
                          const uint32_t (&dst)[IPF]) {
 #pragma unroll
@@ -591,12 +593,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
       unsigned w[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[m][k], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[m][k], true);
-        w[2 * k] = __builtin_bit_cast(unsigned,
-                                      __builtin_convertvector(lo, bf16x2));
-        w[2 * k + 1] = __builtin_bit_cast(unsigned,
-                                          __builtin_convertvector(hi, bf16x2));
+        w[2 * k] = __builtin_bit_cast(
+            unsigned,
+            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[m][k], 1.0f, false));
+        w[2 * k + 1] = __builtin_bit_cast(
+            unsigned,
+            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[m][k], 1.0f, true));
       }
       *reinterpret_cast<u32x4*>(base + dst[m]) = u32x4{w[0], w[1], w[2], w[3]};
       *reinterpret_cast<u32x4*>(base + (dst[m] ^ 16u)) =
