@@ -111,13 +111,14 @@ typedef enum {
  *                       so no partition length is chosen per sequence.
  *   reserved            set to 0 (keeps profile_events 8-byte aligned).
  *   profile_events      a measurement hook, not needed for computing:
- *                       NULL, or two hipEvent_t the call records on
- *                       `stream` immediately before and after the main
- *                       kernel (for pa_decode_append_shared with groups:
- *                       before its first and after its last launch), so
- *                       that a benchmark can time the dominant kernel on
- *                       the stream it runs on.  Recording events serialises
- *                       the stream; leave both NULL in production calls.
+ *                       NULL, or two hipEvent_t that the main kernel's
+ *                       dispatch records at its own start and end (for
+ *                       pa_decode_append_shared with groups: recorded on
+ *                       `stream` before its first and after its last
+ *                       launch), so that a benchmark can time the dominant
+ *                       kernel on the stream it runs on.  Timed dispatches
+ *                       are serialised; leave both NULL in production
+ *                       calls.
  */
 typedef struct {
   int32_t num_seqs;

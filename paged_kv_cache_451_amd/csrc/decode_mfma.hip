@@ -50,6 +50,8 @@
 // of the range) reads a zero tile in device memory instead (idle_tile below).
 #include <math.h>
 
+#include <hip/hip_ext.h>
+
 #include "pa_launch.h"
 
 namespace pa {
@@ -531,8 +533,9 @@ __global__ __launch_bounds__(64, min_waves<D>()) void decode_mfma_kernel(
 
 template <bool FP8, int D>
 void launch_one(const DecodeArgs& a, int nwg, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_mfma_kernel<FP8, D>), dim3(nwg), dim3(64), 0,
-                     stream, reinterpret_cast<const __bf16*>(a.q), a.k_pool,
+  hipExtLaunchKernelGGL((decode_mfma_kernel<FP8, D>), dim3(nwg), dim3(64), 0,
+                        stream, a.ev_start, a.ev_stop, 0,
+                        reinterpret_cast<const __bf16*>(a.q), a.k_pool,
                      a.v_pool, a.block_tables, a.seq_lens,
                      reinterpret_cast<__bf16*>(a.out), a.prefix, a.part_ml,
                      a.part_o, a.direct_ml, a.direct_o, a.s);

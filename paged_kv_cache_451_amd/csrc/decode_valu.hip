@@ -17,6 +17,8 @@
 // used once per call).
 #include <math.h>
 
+#include <hip/hip_ext.h>
+
 #include "pa_launch.h"
 
 namespace pa {
@@ -182,8 +184,9 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
 
 template <int D>
 void launch_one(const DecodeArgs& a, int nwg, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_valu_kernel<D>, dim3(nwg), dim3(64), 0, stream,
-                     reinterpret_cast<const float*>(a.q),
+  hipExtLaunchKernelGGL(decode_valu_kernel<D>, dim3(nwg), dim3(64), 0, stream,
+                        a.ev_start, a.ev_stop, 0,
+                        reinterpret_cast<const float*>(a.q),
                      reinterpret_cast<const float*>(a.k_pool),
                      reinterpret_cast<const float*>(a.v_pool), a.block_tables,
                      a.seq_lens, reinterpret_cast<float*>(a.out), a.prefix,

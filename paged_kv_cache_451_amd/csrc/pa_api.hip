@@ -340,8 +340,10 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
     a.shared_o = so;
     a.shared_splits = p.splits;
   }
-  if (!cascade && ev[0] && hipEventRecord(ev[0], s) != hipSuccess)
-    return PA_ERR_LAUNCH;
+  // outside the cascade step the events ride on the main kernel's own
+  // dispatch: they time the kernel alone, with no packets of their own
+  a.ev_start = cascade ? nullptr : ev[0];
+  a.ev_stop = cascade ? nullptr : ev[1];
   hipError_t e;
   if (desc->kv_dtype == PA_F32)
     e = pa::launch_decode_valu(desc->head_size, a, p.W, s);
@@ -349,8 +351,7 @@ int run_decode(const void* q, const void* k_pool, const void* v_pool,
     e = pa::launch_decode_mfma(desc->kv_dtype == PA_FP8_E4M3FN,
                                desc->head_size, a, p.W, s);
   if (e != hipSuccess) return PA_ERR_LAUNCH;
-  if (!cascade && ev[1] && hipEventRecord(ev[1], s) != hipSuccess)
-    return PA_ERR_LAUNCH;
+  a.ev_start = a.ev_stop = nullptr;
   if (fused) {
     // One query head per merge wave while the whole grid fits on the GPU
     // at once (more loads in flight); two per wave beyond that, so a large

@@ -42,6 +42,10 @@ struct DecodeArgs {
   // Merge pass (plain, or fused without a shared prefix): one workgroup per
   // (sequence, pair of query heads) instead of per (sequence, query head).
   bool merge_pairs;
+  // Measurement hook: when set, the main kernel's dispatch records these
+  // events at its own start and end (no extra packets on the stream).
+  hipEvent_t ev_start;
+  hipEvent_t ev_stop;
   Sched s;
 };
 
