@@ -95,6 +95,11 @@ def parse():
                         "set of distinct slots, one token per block as in a "
                         "decode step) or runs (whole blocks filled in order, "
                         "as a prefill chunk writes them)")
+    p.add_argument("--prefill-budget", type=int, default=0,
+                   help="--op engine: prompt tokens per step (chunked "
+                        "prefill, each chunk attended with pa_prefill); 0 "
+                        "writes whole prompts on admission without prefill "
+                        "attention (the default loop)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the bench, run three plain 1 GiB device "
                         "copies (the reference kernel that scales HBM "
@@ -588,7 +593,10 @@ def bench_engine(a, torch):
 
     rng = np.random.default_rng(a.seed or 0)
     nb = 16384
-    e = Engine(nb, 32, 8, 128, device="cuda:0", seed=a.seed or 0)
+    chunked = a.prefill_budget > 0
+    e = Engine(nb, 32, 8, 128, device="cuda:0", seed=a.seed or 0,
+               max_prefill_tokens=a.prefill_budget if chunked else None,
+               prefill_attention=chunked)
     max_len = 0
     for i in range(1024):
         p = int(rng.integers(128, 2049))
@@ -629,7 +637,13 @@ def bench_engine(a, torch):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "1024 requests, prompts U[128,2048], outputs "
                                "U[64,512], 32/8 heads, D=128, 16384 blocks",
-                   "pool_blocks": nb},
+                   "pool_blocks": nb,
+                   "prefill": (f"chunked, {a.prefill_budget} prompt tokens "
+                               "per step, attended with pa_prefill"
+                               if chunked else "whole prompts written on "
+                               "admission, not attended")},
+        "prefill_tokens_per_s": round(
+            sum(s.prefill_tokens for s in stats) / wall, 1),
         "mean_running": round(float(np.mean(batch)), 1),
         "peak_running": int(max(batch)),
         "contiguous_capacity": contiguous,

@@ -17,7 +17,12 @@ There is no model here: random K/V stand in for the projections of each
 token and random queries for the attention input, so the loop exercises the
 block manager and the device path (``pa_kv_append`` for prompt tokens,
 ``pa_decode_append`` for one new token per running request) at the scale of
-a serving batch.  ``contiguous_capacity`` gives the number of requests a
+a serving batch.  Optionally (``max_prefill_tokens``) a step takes at most
+that many prompt tokens, so a long prompt is cut into chunks spread over
+several steps and mixed with the decode work of the others ("vLLM innenfra",
+continuous-batching paragraph: chunked prefill), and (``prefill_attention``)
+each step's chunks are attended with ``pa_prefill``, the compute-bound side
+of the loop.  ``contiguous_capacity`` gives the number of requests a
 cache that reserves ``max_len`` tokens per request would hold in the same
 pool, for comparison with the concurrency the paged cache reaches.
 
@@ -32,7 +37,12 @@ Readings where the pages leave a step open:
   need for this step's new tokens;
 * every running request decodes one token per step; a request finishes
   after ``max_new_tokens`` decoded tokens and frees its blocks in the same
-  step.
+  step;
+* with chunked prefill, a request takes all its blocks on admission (so
+  admission is priced as before), its prompt tokens are written and attended
+  chunk by chunk in admission order, and it decodes from the step that
+  writes its last prompt token on (that step included, as a whole-prompt
+  admission decodes in its admission step).
 """
 from __future__ import annotations
 
@@ -57,6 +67,7 @@ class Request:
     admitted_step: int = -1
     finished_step: int = -1
     preemptions: int = 0
+    written: int = 0       # tokens of this admission whose K/V are stored
 
     @property
     def num_tokens(self) -> int:
@@ -76,6 +87,7 @@ class StepStats:
     preempted: int
     finished: int
     prefill_tokens: int          # prompt tokens written this step
+    prefill_chunks: int          # requests whose prompt tokens were written
     cached_prefix_tokens: int    # prompt tokens found in the prefix cache
     blocks_used: int
     slots_used: int              # tokens stored in the cache
@@ -101,7 +113,9 @@ class Engine:
     def __init__(self, num_blocks: int, num_q_heads: int, num_kv_heads: int,
                  head_size: int, *, device=None, seed: int = 0,
                  max_running: Optional[int] = None,
-                 prefix_caching: bool = True, mirror: bool = False):
+                 prefix_caching: bool = True, mirror: bool = False,
+                 max_prefill_tokens: Optional[int] = None,
+                 prefill_attention: bool = False):
         self.num_blocks = num_blocks
         self.hq, self.hkv, self.d = num_q_heads, num_kv_heads, head_size
         rng = np.random.default_rng(seed)
@@ -110,6 +124,13 @@ class Engine:
         self.mgr = KVCacheManager(self.pool, BLOCK_SIZE)
         self.max_running = max_running
         self.prefix_caching = prefix_caching
+        if max_prefill_tokens is not None and max_prefill_tokens < 1:
+            raise ValueError("max_prefill_tokens must be at least 1")
+        self.max_prefill_tokens = max_prefill_tokens
+        self.prefill_attention = prefill_attention
+        # the last step's prefill attention, with a mirror: queries (bf16
+        # bits), q_start, tables, lengths, and the device output
+        self.last_prefill = None
         self.waiting: Deque[Request] = deque()
         self.running: List[Request] = []        # in admission order
         self.finished: List[Request] = []
@@ -196,6 +217,7 @@ class Engine:
             assert ok, "an admission that was priced to fit must succeed"
             self.running.append(req)
             self.waiting.popleft()
+            req.written = hits * BLOCK_SIZE
             if req.admitted_step < 0:
                 req.admitted_step = self.step_no
             admitted.append((req, hits * BLOCK_SIZE))
@@ -227,13 +249,33 @@ class Engine:
             return buf[:n]
         return buf[:n], buf[n:2 * n]
 
-    def _write_prompts(self, admitted) -> int:
+    def _prefill_chunks(self) -> List[tuple]:
+        """This step's prompt chunks, (request, first token, end), in
+        admission order, within the prompt-token budget."""
+        budget = self.max_prefill_tokens
+        chunks = []
+        for r in self.running:
+            if r.written >= r.num_tokens:
+                continue
+            n = r.num_tokens - r.written
+            if budget is not None:
+                if budget == 0:
+                    break
+                n = min(n, budget)
+                budget -= n
+            chunks.append((r, r.written, r.written + n))
+        return chunks
+
+    def _write_prompts(self, chunks) -> int:
+        """Writes the chunks' K/V (one append) and, with prefill attention,
+        attends each chunk's tokens to everything stored before them."""
         slots = []
-        for req, cached in admitted:
+        for req, lo, hi in chunks:
             blocks = self.mgr.block_ids(req.req_id)
-            n = req.num_tokens
             slots += [blocks[t // BLOCK_SIZE] * BLOCK_SIZE + t % BLOCK_SIZE
-                      for t in range(cached, n)]
+                      for t in range(lo, hi)]
+        for req, lo, hi in chunks:
+            req.written = hi
         if not slots:
             return 0
         if self.device is None and not self.mirror:
@@ -248,10 +290,38 @@ class Engine:
             _lib.pa_kv_append(k.to(self.device), v.to(self.device),
                               t.from_numpy(slots_np).to(self.device),
                               self.k_pool, self.v_pool)
+        if self.prefill_attention and self.device is not None:
+            self._prefill(chunks, len(slots))
         return len(slots)
+
+    def _prefill(self, chunks, n) -> None:
+        import torch
+        from . import _lib
+        ids = [r.req_id for r, _, _ in chunks]
+        tables, _ = self.mgr.tables(ids)
+        lens = np.asarray([hi for _, _, hi in chunks], dtype=np.int32)
+        q_start = np.concatenate(
+            [[0], np.cumsum([hi - lo for _, lo, hi in chunks])]).astype(
+                np.int32)
+        if self.mirror:
+            g = torch.Generator().manual_seed(int(self.rng.integers(1 << 62)))
+            q = torch.randn(n, self.hq, self.d, generator=g).to(
+                torch.bfloat16)
+        else:
+            q = self._device_rows(n, "q")
+        dev = self.device
+        out = torch.empty(n, self.hq, self.d, dtype=torch.bfloat16,
+                          device=dev)
+        _lib.pa_prefill(q.to(dev), self.k_pool, self.v_pool,
+                        torch.from_numpy(tables).to(dev),
+                        torch.from_numpy(lens).to(dev),
+                        torch.from_numpy(q_start).to(dev), self.scale, out)
+        if self.mirror:
+            self.last_prefill = (q, q_start, tables, lens, out)
 
     def step(self) -> StepStats:
         self.last_writes = []
+        self.last_prefill = None
         preempted = self._ensure_growth()
         admitted = self._admit()
         if not self.running and self.waiting:
@@ -259,9 +329,11 @@ class Engine:
             raise MemoryError(
                 f"request {req.req_id} ({req.num_tokens} tokens) does not fit "
                 f"in an empty pool of {self.num_blocks} blocks")
-        prefill = self._write_prompts(admitted)
+        chunks = self._prefill_chunks()
+        prefill = self._write_prompts(chunks)
         cached = sum(c for _, c in admitted)
-        batch = list(self.running)
+        # requests whose tokens are all stored decode this step
+        batch = [r for r in self.running if r.written >= r.num_tokens]
         finished = 0
         if batch:
             slots = [self.mgr.append_slot(r.req_id,
@@ -274,6 +346,7 @@ class Engine:
             for r, s in zip(batch, slots):
                 tok = self.mgr.req_to_blocks[r.req_id].token_ids
                 r.output_ids.append(tok[-1] if tok else 0)
+                r.written += 1
             still = []
             for r in self.running:
                 if r.done:
@@ -287,7 +360,8 @@ class Engine:
         st = StepStats(
             step=self.step_no, running=len(batch), waiting=len(self.waiting),
             admitted=len(admitted), preempted=preempted, finished=finished,
-            prefill_tokens=prefill, cached_prefix_tokens=cached,
+            prefill_tokens=prefill, prefill_chunks=len(chunks),
+            cached_prefix_tokens=cached,
             blocks_used=self.num_blocks - self.pool.num_free,
             slots_used=sum(self.mgr.req_to_blocks[r.req_id].num_tokens
                            for r in self.running))

@@ -160,3 +160,52 @@ def test_admission_pricing_matches_what_admission_takes():
         before = pool.num_free
         ok, _ = mgr.admit_cached(sid, toks)
         assert ok and before - pool.num_free == price
+
+
+@pytest.mark.parametrize("budget", [1, 37, 256])
+def test_chunked_prefill_writes_each_prompt_token_once(budget):
+    """With a prompt-token budget per step, long prompts are written over
+    several steps in admission order, a request decodes only once all its
+    tokens are stored, no step writes more than the budget, and every
+    request still finishes with its blocks returned (preemptions included)."""
+    rng = np.random.default_rng(11)
+    e = Engine(64, 8, 2, 64, seed=5, prefix_caching=False,
+               max_prefill_tokens=budget)
+    reqs = _requests(rng, 14, prompt=(30, 300), out=(5, 60))
+    for r in reqs:
+        e.add_request(r)
+    spread = 0
+    steps = 0
+    while e.has_work():
+        outs = {r.req_id: len(r.output_ids) for r in reqs}
+        st = e.step()
+        _check_accounting(e)
+        assert st.prefill_tokens <= budget
+        for r in e.running:
+            decoded = len(r.output_ids) - outs[r.req_id]
+            # a request decodes in a step only with all its tokens stored
+            assert r.written == r.num_tokens or decoded == 0
+            assert r.written <= r.num_tokens
+        spread += st.prefill_chunks > 0 and st.running < len(e.running)
+        steps += 1
+        assert steps < 20_000
+    assert len(e.finished) == 14
+    assert all(len(r.output_ids) == r.max_new_tokens for r in reqs)
+    assert e.pool.num_free == 64 and not e.mgr.req_to_blocks
+    if budget < 300:
+        assert spread > 0   # some prompt was still being written
+
+
+def test_unbounded_budget_keeps_whole_prompt_admission():
+    """max_prefill_tokens=None is the whole-prompt loop: the same steps and
+    statistics as an engine built without it."""
+    rng = np.random.default_rng(12)
+    reqs = _requests(rng, 20)
+    a = Engine(128, 8, 2, 64, seed=9)
+    b = Engine(128, 8, 2, 64, seed=9, max_prefill_tokens=None)
+    for r in reqs:
+        a.add_request(Request(r.req_id, list(r.prompt_ids), r.max_new_tokens))
+        b.add_request(Request(r.req_id, list(r.prompt_ids), r.max_new_tokens))
+    while a.has_work() or b.has_work():
+        sa, sb = a.step(), b.step()
+        assert sa == sb
