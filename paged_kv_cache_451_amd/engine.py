@@ -211,7 +211,13 @@ class Engine:
             if take + self._growth_need() + grow > self.pool.num_free:
                 break
             if self.prefix_caching:
-                ok, hits = self.mgr.admit_cached(req.req_id, ids)
+                # a prompt written over several steps registers its blocks
+                # in the prefix cache as their KV is written, so that a
+                # later admission (its own after a preemption included)
+                # never finds a block that holds no KV yet
+                ok, hits = self.mgr.admit_cached(
+                    req.req_id, ids,
+                    register=self.max_prefill_tokens is None)
             else:
                 ok, hits = self.mgr.admit(req.req_id, len(ids)), 0
             assert ok, "an admission that was priced to fit must succeed"
@@ -276,6 +282,8 @@ class Engine:
                       for t in range(lo, hi)]
         for req, lo, hi in chunks:
             req.written = hi
+            if self.prefix_caching and self.max_prefill_tokens is not None:
+                self.mgr.cache_written(req.req_id, hi)
         if not slots:
             return 0
         if self.device is None and not self.mirror:

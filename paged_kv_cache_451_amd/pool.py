@@ -209,6 +209,9 @@ class SeqState:
     num_tokens: int = 0  # tokens already stored in the cache
     blocks: List[KVCacheBlock] = field(default_factory=list)
     token_ids: Optional[List[int]] = None  # kept when prefix caching is used
+    # (block index, key) of fresh full blocks admitted without registering
+    # them, in order; cache_written registers them once their KV is stored
+    pending_keys: List[Tuple[int, int]] = field(default_factory=list)
 
 
 class KVCacheManager:
@@ -282,15 +285,18 @@ class KVCacheManager:
         fresh = self.blocks_needed(len(toks)) - len(hits)
         return fresh + sum(1 for b in hits if b.ref_cnt == 0)
 
-    def admit_cached(self, seq_id: int,
-                     token_ids: Sequence[int]) -> Tuple[bool, int]:
+    def admit_cached(self, seq_id: int, token_ids: Sequence[int],
+                     register: bool = True) -> Tuple[bool, int]:
         """Admit a request whose tokens are known, reusing cached full
         blocks of an identical prefix.  Returns (admitted, cached blocks
         reused); the reused blocks' KV is already in the pool, only the rest
         must be written.  Fresh full blocks are registered in the cache at
         once, so the caller must write their KV before the next admission
         can find them (a caller that may undo an admission checks
-        ``blocks_to_admit`` first instead of undoing it)."""
+        ``blocks_to_admit`` first instead of undoing it).  With
+        ``register=False`` they are registered only by ``cache_written``,
+        for a caller that writes a prompt over several steps and may free
+        the request before all of it is written."""
         if seq_id in self.req_to_blocks:
             raise ValueError(f"sequence {seq_id} already admitted")
         toks = [int(t) for t in token_ids]
@@ -311,10 +317,25 @@ class KVCacheManager:
             state.blocks.append(blk)
             j = len(hits) + i
             if j < nfull:
-                self.pool.cache(blk, hashes[j])
+                if register:
+                    self.pool.cache(blk, hashes[j])
+                else:
+                    state.pending_keys.append((j, hashes[j]))
         state.num_tokens = len(toks)
         self.req_to_blocks[seq_id] = state
         return True, len(hits)
+
+    def cache_written(self, seq_id: int, num_tokens: int) -> None:
+        """Registers the pending full blocks that lie within the first
+        ``num_tokens`` tokens of the sequence, whose KV is now stored."""
+        st = self.req_to_blocks[seq_id]
+        done = num_tokens // self.block_size
+        k = 0
+        while k < len(st.pending_keys) and st.pending_keys[k][0] < done:
+            idx, key = st.pending_keys[k]
+            self.pool.cache(st.blocks[idx], key)
+            k += 1
+        del st.pending_keys[:k]
 
     def fork(self, src_id: int, new_id: int) -> None:
         """A new sequence continuing src's context: it shares every block

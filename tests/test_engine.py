@@ -209,3 +209,89 @@ def test_unbounded_budget_keeps_whole_prompt_admission():
     while a.has_work() or b.has_work():
         sa, sb = a.step(), b.step()
         assert sa == sb
+
+
+def _content_keys(ids):
+    """Key of each position's K/V: a causal model's K/V at position t
+    depends on tokens 0..t, so the key chains the ids up to t."""
+    keys, k = [], 0
+    for t in ids:
+        k = hash((k, int(t)))
+        keys.append(k)
+    return keys
+
+
+def _watch_contents(e):
+    """Wraps the engine's writes so that every slot's content key is
+    tracked; every prompt chunk and every decode then checks that all the
+    context it attends holds the keys of its own tokens.  Returns the list
+    of violations found."""
+    held = {}                  # slot -> content key
+    bad = []
+
+    def slots_of(rid, lo, hi):
+        blocks = e.mgr.block_ids(rid)
+        return [blocks[t // 16] * 16 + t % 16 for t in range(lo, hi)]
+
+    def check(rid, ids, n, what):
+        keys = _content_keys(ids[:n])
+        for t, s in enumerate(slots_of(rid, 0, n)):
+            if held.get(s) != keys[t]:
+                bad.append((e.step_no, what, rid, t))
+                return
+
+    write_prompts, decode = e._write_prompts, e._decode
+
+    def spy_write(chunks):
+        for req, lo, hi in chunks:
+            ids = req.prompt_ids + req.output_ids
+            check(req.req_id, ids, lo, "prefill")
+            keys = _content_keys(ids[:hi])
+            for t, s in zip(range(lo, hi), slots_of(req.req_id, lo, hi)):
+                held[s] = keys[t]
+        return write_prompts(chunks)
+
+    def spy_decode(batch, slots):
+        for r, s in zip(batch, slots):
+            ids = e.mgr.req_to_blocks[r.req_id].token_ids
+            check(r.req_id, ids, len(ids) - 1, "decode")
+            held[s] = _content_keys(ids)[-1]
+        return decode(batch, slots)
+
+    e._write_prompts, e._decode = spy_write, spy_decode
+    return bad
+
+
+@pytest.mark.parametrize("budget,num_blocks",
+                         [(None, 32), (1, 24), (1, 48), (3, 32), (3, 48),
+                          (24, 32)])
+def test_every_step_attends_written_kv_only(budget, num_blocks):
+    """With the prefix cache on, shared prompt prefixes and a pool small
+    enough to preempt requests (also in the middle of their prompts), every
+    prompt chunk and every decode attends only slots that hold the K/V of
+    its own tokens: a cached block is found only once its K/V is written
+    (a chunked prompt registers its blocks as they are written, so a
+    request preempted mid-prompt leaves no key to an unwritten block)."""
+    rng = np.random.default_rng(4)
+    system = rng.integers(0, 1000, size=96).tolist()
+    reqs = []
+    for i in range(12):
+        head = system if i % 2 else system[:48]
+        reqs.append(Request(i, head + rng.integers(
+            0, 1000, size=int(rng.integers(10, 120))).tolist(),
+            int(rng.integers(5, 60))))
+    e = Engine(num_blocks, 8, 2, 64, seed=4, max_prefill_tokens=budget)
+    bad = _watch_contents(e)
+    for r in reqs:
+        e.add_request(r)
+    pre = hits = steps = 0
+    while e.has_work():
+        st = e.step()
+        _check_accounting(e)
+        pre += st.preempted
+        hits += st.cached_prefix_tokens
+        steps += 1
+        assert steps < 20_000
+    assert not bad, bad[:5]
+    assert pre > 0 and hits > 0
+    assert len(e.finished) == 12

@@ -160,6 +160,29 @@ def test_prefix_cache_hits_in_the_free_queue_are_not_double_booked():
     assert mgr.admit_cached(1, list(range(32)) + [1] * 10) == (True, 2)
 
 
+def test_deferred_registration_caches_written_blocks_only():
+    """admit_cached(register=False) registers a fresh full block only when
+    cache_written reports its tokens stored: a request freed with part of
+    its prompt unwritten leaves keys to the written blocks alone."""
+    pool = BlockPool(8, order=range(8))
+    mgr = KVCacheManager(pool, 16)
+    prompt = list(range(100, 160))            # 3 full blocks + 12 tokens
+    assert mgr.admit_cached(0, prompt, register=False) == (True, 0)
+    assert pool.cached_block_hash_to_block == {}
+    mgr.cache_written(0, 31)                  # block 0 written, 1 not yet
+    assert len(pool.cached_block_hash_to_block) == 1
+    mgr.cache_written(0, 40)
+    assert len(pool.cached_block_hash_to_block) == 2
+    ids = mgr.block_ids(0)
+    mgr.free_seq(0)                           # preempted mid-prompt
+    ok, hits = mgr.admit_cached(1, prompt, register=False)
+    assert ok and hits == 2 and mgr.block_ids(1)[:2] == ids[:2]
+    mgr.cache_written(1, 60)                  # the whole prompt now
+    assert len(pool.cached_block_hash_to_block) == 3
+    assert not mgr.req_to_blocks[1].pending_keys
+    assert mgr.admit_cached(2, prompt[:48]) == (True, 3)
+
+
 def test_fcfs_admission_reproduces_capacity_example():
     ex = json.load(open(os.path.join(GOLDEN, "capacity_example.json")))
     pool = BlockPool(ex["pool"])
