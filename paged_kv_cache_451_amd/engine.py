@@ -68,6 +68,9 @@ class Request:
     finished_step: int = -1
     preemptions: int = 0
     written: int = 0       # tokens of this admission whose K/V are stored
+    # (token count, prefix-cache keys of its full blocks), computed once
+    # for the tokens a waiting request is priced and admitted with
+    keys: Optional[tuple] = field(default=None, repr=False, compare=False)
 
     @property
     def num_tokens(self) -> int:
@@ -205,7 +208,12 @@ class Engine:
             # admission that registered its fresh blocks in the cache and
             # was then undone would leave keys to blocks that never
             # received their KV).
-            take = (self.mgr.blocks_to_admit(ids) if self.prefix_caching
+            keys = None
+            if self.prefix_caching:
+                if req.keys is None or req.keys[0] != len(ids):
+                    req.keys = (len(ids), self.mgr.prefix_keys(ids))
+                keys = req.keys[1]
+            take = (self.mgr.blocks_to_admit(ids, keys) if self.prefix_caching
                     else self.mgr.blocks_needed(len(ids)))
             grow = 1 if len(ids) % BLOCK_SIZE == 0 else 0
             if take + self._growth_need() + grow > self.pool.num_free:
@@ -217,7 +225,7 @@ class Engine:
                 # never finds a block that holds no KV yet
                 ok, hits = self.mgr.admit_cached(
                     req.req_id, ids,
-                    register=self.max_prefill_tokens is None)
+                    register=self.max_prefill_tokens is None, keys=keys)
             else:
                 ok, hits = self.mgr.admit(req.req_id, len(ids)), 0
             assert ok, "an admission that was priced to fit must succeed"
@@ -344,10 +352,9 @@ class Engine:
         batch = [r for r in self.running if r.written >= r.num_tokens]
         finished = 0
         if batch:
-            slots = [self.mgr.append_slot(r.req_id,
-                                          token_id=int(self.rng.integers(
-                                              1 << 17)))
-                     for r in batch]
+            tokens = self.rng.integers(1 << 17, size=len(batch)).tolist()
+            slots = [self.mgr.append_slot(r.req_id, token_id=t)
+                     for r, t in zip(batch, tokens)]
             copies = self.mgr.take_copies()
             assert not copies, "running requests never share a partial block"
             self._decode(batch, slots)

@@ -260,14 +260,25 @@ class KVCacheManager:
         self.req_to_blocks[seq_id] = state
         return True
 
-    def _cached_prefix(self, toks: Sequence[int]):
-        """Keys of the full blocks of ``toks`` and the cached blocks of its
-        longest cached prefix (lookups stop at the first miss)."""
+    def prefix_keys(self, token_ids: Sequence[int]) -> List[int]:
+        """Keys of the full blocks of ``token_ids``, in order (each chained
+        to the one before); a caller that prices and admits the same tokens
+        more than once can compute them once and pass them in."""
         bs = self.block_size
-        hashes, parent = [], 0
+        toks = [int(t) for t in token_ids]
+        keys, parent = [], 0
         for i in range(len(toks) // bs):
             parent = hash_block_tokens(parent, toks[i * bs:(i + 1) * bs])
-            hashes.append(parent)
+            keys.append(parent)
+        return keys
+
+    def _cached_prefix(self, toks: Sequence[int],
+                       keys: Optional[List[int]] = None):
+        """Keys of the full blocks of ``toks`` and the cached blocks of its
+        longest cached prefix (lookups stop at the first miss)."""
+        hashes = self.prefix_keys(toks) if keys is None else keys
+        if len(hashes) != len(toks) // self.block_size:
+            raise ValueError("keys do not match the tokens' full blocks")
         hits: List[KVCacheBlock] = []
         for h in hashes:
             blk = self.pool.lookup(h)
@@ -276,17 +287,19 @@ class KVCacheManager:
             hits.append(blk)
         return hashes, hits
 
-    def blocks_to_admit(self, token_ids: Sequence[int]) -> int:
+    def blocks_to_admit(self, token_ids: Sequence[int],
+                        keys: Optional[List[int]] = None) -> int:
         """Free-queue blocks ``admit_cached(token_ids)`` would take: its
         fresh blocks plus the cached hits that sit in the free queue (a
-        touch takes them out of it).  Reserves nothing."""
-        toks = [int(t) for t in token_ids]
-        _, hits = self._cached_prefix(toks)
-        fresh = self.blocks_needed(len(toks)) - len(hits)
+        touch takes them out of it).  Reserves nothing.  ``keys``, if
+        given, are ``prefix_keys(token_ids)``."""
+        _, hits = self._cached_prefix(token_ids, keys)
+        fresh = self.blocks_needed(len(token_ids)) - len(hits)
         return fresh + sum(1 for b in hits if b.ref_cnt == 0)
 
     def admit_cached(self, seq_id: int, token_ids: Sequence[int],
-                     register: bool = True) -> Tuple[bool, int]:
+                     register: bool = True,
+                     keys: Optional[List[int]] = None) -> Tuple[bool, int]:
         """Admit a request whose tokens are known, reusing cached full
         blocks of an identical prefix.  Returns (admitted, cached blocks
         reused); the reused blocks' KV is already in the pool, only the rest
@@ -296,12 +309,13 @@ class KVCacheManager:
         ``blocks_to_admit`` first instead of undoing it).  With
         ``register=False`` they are registered only by ``cache_written``,
         for a caller that writes a prompt over several steps and may free
-        the request before all of it is written."""
+        the request before all of it is written.  ``keys``, if given, are
+        ``prefix_keys(token_ids)``."""
         if seq_id in self.req_to_blocks:
             raise ValueError(f"sequence {seq_id} already admitted")
         toks = [int(t) for t in token_ids]
         nfull = len(toks) // self.block_size
-        hashes, hits = self._cached_prefix(toks)
+        hashes, hits = self._cached_prefix(toks, keys)
         # a hit that sits in the free queue still counts as free until
         # touched: it must not be allocated for this request's fresh blocks
         fresh = self.blocks_needed(len(toks)) - len(hits)

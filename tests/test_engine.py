@@ -157,8 +157,12 @@ def test_admission_pricing_matches_what_admission_takes():
                       (3, rng.integers(0, 1000, 40).tolist()),  # misses
                       (4, base[:32])]:                          # all hits
         price = mgr.blocks_to_admit(toks)
+        keys = mgr.prefix_keys(toks)
+        assert mgr.blocks_to_admit(toks, keys) == price
+        with pytest.raises(ValueError):
+            mgr.blocks_to_admit(toks + [0] * 16, keys)
         before = pool.num_free
-        ok, _ = mgr.admit_cached(sid, toks)
+        ok, _ = mgr.admit_cached(sid, toks, keys=keys)
         assert ok and before - pool.num_free == price
 
 
