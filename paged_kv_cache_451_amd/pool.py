@@ -212,6 +212,9 @@ class SeqState:
     # (block index, key) of fresh full blocks admitted without registering
     # them, in order; cache_written registers them once their KV is stored
     pending_keys: List[Tuple[int, int]] = field(default_factory=list)
+    # int32 ids of ``blocks``, rebuilt after the list changes (None then)
+    ids: Optional[np.ndarray] = field(default=None, repr=False,
+                                      compare=False)
 
 
 class KVCacheManager:
@@ -394,6 +397,7 @@ class KVCacheManager:
             if blk is None:
                 raise MemoryError("KV block pool exhausted")
             st.blocks.append(blk)
+            st.ids = None
         idx = st.num_tokens // bs
         last = st.blocks[idx]
         if last.ref_cnt > 1:
@@ -403,6 +407,7 @@ class KVCacheManager:
             self.pending_copies.append((last.block_id, copy.block_id))
             self.pool.free(last)
             st.blocks[idx] = copy
+            st.ids = None
             last = copy
         slot = last.block_id * bs + st.num_tokens % bs
         st.num_tokens += 1
@@ -432,14 +437,23 @@ class KVCacheManager:
                width: Optional[int] = None):
         """int32 ``block_tables`` [B, width] (padded with ``pad``) and
         ``seq_lens`` [B] for ``seq_ids`` in that order."""
-        rows = [self.block_ids(s) for s in seq_ids]
-        w = max((len(r) for r in rows), default=0) if width is None else width
+        states = [self.req_to_blocks[s] for s in seq_ids]
+        rows = []
+        for st in states:
+            if st.ids is None:
+                st.ids = np.fromiter((b.block_id for b in st.blocks),
+                                     dtype=np.int32, count=len(st.blocks))
+            rows.append(st.ids)
+        n = np.fromiter((len(r) for r in rows), dtype=np.int64,
+                        count=len(rows))
+        w = int(n.max(initial=0)) if width is None else width
         w = max(w, 1)
+        if len(rows) and int(n.max()) > w:
+            raise ValueError("table width too small")
         table = np.full((len(rows), w), pad, dtype=np.int32)
-        for i, r in enumerate(rows):
-            if len(r) > w:
-                raise ValueError("table width too small")
-            table[i, :len(r)] = r
-        lens = np.array([self.req_to_blocks[s].num_tokens for s in seq_ids],
-                        dtype=np.int32)
+        if len(rows):
+            # row-major order of the mask is the order of the rows' ids
+            table[np.arange(w) < n[:, None]] = np.concatenate(rows)
+        lens = np.fromiter((st.num_tokens for st in states), dtype=np.int32,
+                           count=len(states))
         return table, lens

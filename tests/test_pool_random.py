@@ -15,7 +15,8 @@ frequent, and after each step checks:
 * each request holds exactly ceil(tokens / 16) blocks;
 * the slot an append returns lies in a block that only that request
   references, at the request's token position;
-* the prefix cache maps every key to a block that carries that key.
+* the prefix cache maps every key to a block that carries that key;
+* the block tables name each request's blocks in order, padded with -1.
 """
 import numpy as np
 import pytest
@@ -43,6 +44,17 @@ def check_invariants(mgr: KVCacheManager) -> None:
     assert pool.num_free == sum(1 for b in pool.blocks if b.ref_cnt == 0)
     for h, blk in pool.cached_block_hash_to_block.items():
         assert blk.block_hash == h
+    # the device tables name every request's blocks in order, padded
+    ids = list(mgr.req_to_blocks)
+    rng = np.random.default_rng(len(ids))
+    ids = [ids[i] for i in rng.permutation(len(ids))]
+    table, lens = mgr.tables(ids)
+    for i, sid in enumerate(ids):
+        st = mgr.req_to_blocks[sid]
+        row = [b.block_id for b in st.blocks]
+        assert table[i, :len(row)].tolist() == row
+        assert (table[i, len(row):] == -1).all()
+        assert lens[i] == st.num_tokens
 
 
 def _random_walk(seed: int, steps: int, num_blocks: int) -> dict:
