@@ -216,3 +216,49 @@ def test_shared_prefix_step_counts(prefix_len):
     out, dev = run_shared(case, [0, cfg.num_seqs], [prefix_len // 16])
     assert max_err(out, oracle_ref(case)) <= TOL
     assert_pools_appended(case, dev)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_dominant_key_probes_across_the_prefix_boundary(kv_dtype):
+    """Which key each sequence reads, made visible around the seam of the
+    cascade: a query of ±1 signs and one key equal to a large multiple of
+    it give that key a weight of 1 up to rounding, so each output must be
+    that key's V row (a closed form, checked without the oracle).  Probed
+    positions: the first and last shared tokens, the first slot of the
+    last shared block, the first own token, the slot before the newest
+    token, the newest token's block start and the newest token itself
+    (whose K/V the step appends)."""
+    case = small_prefix_case(seed=3, kv_dtype=kv_dtype)
+    fp8 = kv_dtype == "fp8_e4m3fn"
+    p = 512
+    lens = case.seq_lens.numpy()
+    tabs = case.block_tables.numpy()
+    hkv, d = case.k_pool.shape[1], case.k_pool.shape[3]
+    rng = np.random.default_rng(9)
+    vs = case.v_scale if fp8 else 1.0
+    probes = []
+    for b in range(8):
+        last = int(lens[b]) - 1         # the newest token, appended here
+        assert last > p + 1             # every sequence has own tokens
+        t = [p - 1, p, last, last - 1, 0, p - 16, last - last % 16,
+             last][b]
+        u = torch.from_numpy(rng.choice([-1.0, 1.0], size=d)).float()
+        case.q[b] = u.to(case.q.dtype)
+        key = ((448.0 if fp8 else 16.0) * u).to(case.k_pool.dtype)
+        if t == last:
+            case.k_new[b] = key
+            v = case.v_new[b].to(torch.float64) * vs
+        else:
+            blk = tabs[b, t // 16]
+            case.k_pool[blk, :, t % 16] = key
+            v = case.v_pool[blk, :, :, t % 16].to(torch.float64) * vs
+        probes.append((b, t, v))
+    out, dev = run_shared(case, [0, 8], [p // 16])
+    tol = TOL_FP8 if fp8 else TOL
+    assert max_err(out, oracle_ref(case)) <= tol
+    assert_pools_appended(case, dev)
+    g_of = np.arange(case.q.shape[1]) // (case.q.shape[1] // hkv)
+    got = out.cpu().to(torch.float64)
+    for b, t, v in probes:
+        err = (got[b] - v[g_of]).abs().max().item()
+        assert err <= tol, (b, t, err)

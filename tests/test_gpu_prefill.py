@@ -264,3 +264,83 @@ def test_fp8_prefill_widens_every_code_exactly(gpu_lib):
         np.stack([v[b, 0, :, 0] for b in range(nb)]))
     got = out.cpu().to(torch.float64).numpy()
     assert np.array_equal(got, np.repeat(expect[:, None, :], hq, axis=1))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_dominant_key_probes_at_the_causal_edge(gpu_lib, kv_dtype):
+    """Which key each query token reads, made visible: a query row u (signs
+    of ±1) and one key equal to a large multiple of u at a chosen position
+    give that key a weight of 1 up to rounding, so the output is that key's
+    V row (a closed form, checked without the oracle) when the position is
+    attended, and far from it when the position lies after the query token
+    (the causal mask).  Positions probed: the query's own position, the
+    next one, the previous one, its block's first slot, the slot before it
+    and position 0.  Every output also matches the oracle."""
+    case = build_prefill_case(cfg(num_seqs=3, prior_lo=30, prior_hi=200,
+                                  kv_dtype=kv_dtype), seed=29,
+                              chunks=[70, 33, 130])
+    rng = np.random.default_rng(5)
+    qs, lens = case.q_start.numpy(), case.seq_lens.numpy()
+    tabs = case.block_tables.numpy()
+    hkv, d = case.k_pool.shape[1], case.k_pool.shape[3]
+    fp8 = kv_dtype == "fp8_e4m3fn"
+    probes = []                           # (row, kv block, offset, masked)
+    for b in range(3):
+        n, c = int(lens[b]), int(qs[b + 1] - qs[b])
+        taken = set()
+        for j, i in enumerate(sorted({0, c // 5, 2 * c // 5, 3 * c // 5,
+                                      4 * c // 5, c - 1})):
+            pos = n - c + i
+            first = pos - pos % 16
+            kinds = (pos, pos + 1, pos - 1, first, first - 1, 0)
+            for t in kinds[j:] + kinds[:j]:
+                if 0 <= t < n and t not in taken:
+                    break
+            else:
+                continue
+            taken.add(t)
+            u = torch.from_numpy(rng.choice([-1.0, 1.0], size=d)).float()
+            case.q[qs[b] + i] = u.to(torch.bfloat16)
+            key = (448.0 if fp8 else 16.0) * u
+            for g in range(hkv):
+                case.k_pool[tabs[b, t // 16], g, t % 16] = key.to(
+                    case.k_pool.dtype)
+            probes.append((qs[b] + i, tabs[b, t // 16], t % 16, t > pos))
+    assert len(probes) == 18 and sum(m for *_, m in probes) >= 3
+    out = run(case)
+    ref = oracle.paged_prefill(**prefill_args(case))
+    assert max_err(out, ref) <= TOL
+    g_of = np.arange(case.q.shape[1]) // (case.q.shape[1] // hkv)
+    vs = case.v_scale if fp8 else 1.0
+    for row, blk, off, masked in probes:
+        v = case.v_pool[blk, :, :, off].to(torch.float64) * vs   # [Hkv, D]
+        err = (out[row].to(torch.float64) - v[g_of]).abs().max().item()
+        if masked:
+            assert err > 0.5, (row, blk, off)
+        else:
+            assert err <= TOL, (row, blk, off, err)
+
+
+def test_scores_that_keep_growing_along_the_keys(gpu_lib):
+    """Keys that drift towards every query (scores rising by about 5 log2
+    units per 64-key step, 60 over the context, on top of scores 4x the
+    usual spread): the running maximum grows step after step, so the
+    kernel's rescaling of its accumulators runs again and again and the
+    probabilities stay far from 1 until the last steps."""
+    case = build_prefill_case(cfg(num_seqs=2, prior_lo=600, prior_hi=800),
+                              seed=31, chunks=[64, 100])
+    d = case.k_pool.shape[3]
+    qs, lens = case.q_start.numpy(), case.seq_lens.numpy()
+    tabs = case.block_tables.numpy()
+    rng = np.random.default_rng(7)
+    for b in range(2):
+        u = torch.from_numpy(rng.choice([-1.0, 1.0], size=d)).float()
+        q = case.q[qs[b]:qs[b + 1]].float()
+        case.q[qs[b]:qs[b + 1]] = (4 * q + 2 * u).to(torch.bfloat16)
+        for t in range(int(lens[b])):
+            blk = tabs[b, t // 16]
+            k = case.k_pool[blk, :, t % 16].float() + 0.0024 * t * u
+            case.k_pool[blk, :, t % 16] = k.to(torch.bfloat16)
+    out = run(case)
+    ref = oracle.paged_prefill(**prefill_args(case))
+    assert max_err(out, ref) <= TOL
