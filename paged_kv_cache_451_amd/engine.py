@@ -302,23 +302,39 @@ class Engine:
             self._record_write(k, v, slots_np)
         if self.device is not None:
             from . import _lib
-            t = self.torch
+            ints = [slots_np]
+            if self.prefill_attention:
+                ids = [r.req_id for r, _, _ in chunks]
+                tables, _ = self.mgr.tables(ids)
+                lens = np.asarray([hi for _, _, hi in chunks], dtype=np.int32)
+                q_start = np.concatenate(
+                    [[0], np.cumsum([hi - lo for _, lo, hi in chunks])]
+                ).astype(np.int32)
+                ints += [tables, lens, q_start]
+            dev_ints = self._upload(*ints)
             _lib.pa_kv_append(k.to(self.device), v.to(self.device),
-                              t.from_numpy(slots_np).to(self.device),
-                              self.k_pool, self.v_pool)
-        if self.prefill_attention and self.device is not None:
-            self._prefill(chunks, len(slots))
+                              dev_ints[0], self.k_pool, self.v_pool)
+            if self.prefill_attention:
+                self._prefill(len(slots), ints[1:], dev_ints[1:])
         return len(slots)
 
-    def _prefill(self, chunks, n) -> None:
+    def _upload(self, *arrays):
+        """One host-to-device copy of several int32 arrays; returns their
+        device views in order, each starting on a 64-byte boundary."""
+        sizes = [a.size for a in arrays]
+        offs = np.cumsum([0] + [-(-n // 16) * 16 for n in sizes])
+        flat = np.zeros(int(offs[-1]), dtype=np.int32)
+        for a, o in zip(arrays, offs):
+            flat[o:o + a.size] = a.ravel()
+        buf = self.torch.from_numpy(flat).to(self.device)
+        return [buf[o:o + a.size].view(a.shape) for a, o in zip(arrays, offs)]
+
+    def _prefill(self, n, host, dev_ints) -> None:
+        """pa_prefill over the step's chunks: ``host`` holds their tables,
+        lengths and query starts, ``dev_ints`` the same on the device."""
         import torch
         from . import _lib
-        ids = [r.req_id for r, _, _ in chunks]
-        tables, _ = self.mgr.tables(ids)
-        lens = np.asarray([hi for _, _, hi in chunks], dtype=np.int32)
-        q_start = np.concatenate(
-            [[0], np.cumsum([hi - lo for _, lo, hi in chunks])]).astype(
-                np.int32)
+        tables, lens, q_start = host
         if self.mirror:
             g = torch.Generator().manual_seed(int(self.rng.integers(1 << 62)))
             q = torch.randn(n, self.hq, self.d, generator=g).to(
@@ -328,10 +344,8 @@ class Engine:
         dev = self.device
         out = torch.empty(n, self.hq, self.d, dtype=torch.bfloat16,
                           device=dev)
-        _lib.pa_prefill(q.to(dev), self.k_pool, self.v_pool,
-                        torch.from_numpy(tables).to(dev),
-                        torch.from_numpy(lens).to(dev),
-                        torch.from_numpy(q_start).to(dev), self.scale, out)
+        _lib.pa_prefill(q.to(dev), self.k_pool, self.v_pool, *dev_ints,
+                        self.scale, out)
         if self.mirror:
             self.last_prefill = (q, q_start, tables, lens, out)
 
@@ -408,11 +422,10 @@ class Engine:
         dev = self.device
         out = torch.empty(n, self.hq, self.d, dtype=torch.bfloat16,
                           device=dev)
-        args = (q.to(dev), self.k_pool, self.v_pool,
-                torch.from_numpy(tables).to(dev),
-                torch.from_numpy(lens.astype(np.int32)).to(dev), self.scale,
-                out, kn.to(dev), vn.to(dev),
-                torch.from_numpy(np.asarray(slots, dtype=np.int32)).to(dev))
+        d_tables, d_lens, d_slots = self._upload(
+            tables, lens.astype(np.int32), np.asarray(slots, dtype=np.int32))
+        args = (q.to(dev), self.k_pool, self.v_pool, d_tables, d_lens,
+                self.scale, out, kn.to(dev), vn.to(dev), d_slots)
         desc = _lib.decode_desc(args[0], self.k_pool, args[3],
                                 max_seq_len=int(lens.max()),
                                 total_blocks_hint=int(((lens + 15) // 16)

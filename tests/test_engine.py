@@ -299,3 +299,22 @@ def test_every_step_attends_written_kv_only(budget, num_blocks):
     assert not bad, bad[:5]
     assert pre > 0 and hits > 0
     assert len(e.finished) == 12
+
+
+def test_one_upload_carries_every_int_array_of_a_step():
+    """The step's tables, lengths and slots go to the device in one copy:
+    each comes back with its shape and values, contiguous, 64-byte apart."""
+    import torch
+    e = Engine(8, 2, 1, 64)
+    e.torch, e.device = torch, "cpu"
+    a = np.arange(35, dtype=np.int32).reshape(5, 7)
+    b = np.array([3], dtype=np.int32)
+    c = np.zeros(0, dtype=np.int32)
+    d = np.arange(20, dtype=np.int32)
+    ta, tb, tc, td = e._upload(a, b, c, d)
+    assert ta.shape == (5, 7) and np.array_equal(ta.numpy(), a)
+    assert tb.tolist() == [3] and tc.numel() == 0
+    assert np.array_equal(td.numpy(), d)
+    for t in (ta, tb, td):
+        assert t.is_contiguous() and t.dtype == torch.int32
+        assert (t.data_ptr() - ta.data_ptr()) % 64 == 0
