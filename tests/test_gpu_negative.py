@@ -118,3 +118,130 @@ def test_planted_mistake_breaks_parity(gpu_lib, mistake, fused):
     if not fused:
         # the device computed exactly the mistaken input
         assert np.abs(got - _oracle(case, **oracle_kw)).max() <= TOL
+
+
+# -- chunked prefill ----------------------------------------------------------
+
+def _prefill_case():
+    from paged_kv_cache_451_amd.workloads import PREFILL_BY_NAME, \
+        build_prefill_case
+    cfg = PREFILL_BY_NAME["prefill_llama3_8b_bf16"].replace(
+        num_seqs=4, prior_lo=0, prior_hi=60)
+    return build_prefill_case(cfg, seed=27, chunks=[1, 5, 40, 100])
+
+
+def _prefill_mistakes(case):
+    """name -> inputs that differ from the case's (numpy arrays)."""
+    lens = case.seq_lens.numpy()
+    qs = case.q_start.numpy()
+    tab = case.block_tables.numpy().copy()
+    tab[2, 0] = tab[3, 1]             # a sequence reads a foreign block
+    hq = case.q.shape[1]
+    g = hq // case.k_pool.shape[1]
+    perm = np.array([(h + g) % hq for h in range(hq)])
+    q_bits = case.q.view(torch.int16).numpy()
+    moved = qs.copy()
+    moved[2] += 1                     # a token moved to the next chunk
+    return {
+        "length off by one": dict(seq_lens=(lens - 1).astype(np.int32)),
+        "chunk boundary off by one": dict(q_start=moved),
+        "foreign block in the table": dict(block_tables=tab),
+        "query heads in other KV groups": dict(
+            q=np.ascontiguousarray(q_bits[:, perm])),
+        "scale dropped": dict(scale=1.0),
+    }
+
+
+def _prefill_oracle(case, change):
+    from conftest import prefill_args
+    args = prefill_args(case)
+    for k, v in change.items():
+        args[k] = v.view(np.uint16) if k == "q" else v
+    return oracle.paged_prefill(**args)
+
+
+def _prefill_device(case, change):
+    from paged_kv_cache_451_amd import _lib
+    dev = {k: getattr(case, k).cuda() for k in
+           ("q", "k_pool", "v_pool", "block_tables", "seq_lens", "q_start")}
+    for k, v in change.items():
+        if k == "q":
+            dev["q"] = torch.from_numpy(v).view(torch.bfloat16).cuda()
+        elif k != "scale":
+            dev[k] = torch.from_numpy(v).cuda()
+    out = torch.full_like(dev["q"], float("nan"))
+    _lib.pa_prefill(dev["q"], dev["k_pool"], dev["v_pool"],
+                    dev["block_tables"], dev["seq_lens"], dev["q_start"],
+                    change.get("scale", case.scale), out)
+    torch.cuda.synchronize()
+    g = out.cpu().to(torch.float64).numpy()
+    assert np.isfinite(g).all()
+    return g
+
+
+@pytest.mark.parametrize("mistake", ["length off by one",
+                                     "chunk boundary off by one",
+                                     "foreign block in the table",
+                                     "query heads in other KV groups",
+                                     "scale dropped"])
+def test_planted_prefill_mistake_breaks_parity(gpu_lib, mistake):
+    """The same controls for chunked prefill (plus a query token moved
+    across a chunk boundary): the device computes the mistaken input as
+    given and misses the correct oracle by more than 10x the tolerance."""
+    case = _prefill_case()
+    ref = _prefill_oracle(case, {})
+    assert np.abs(_prefill_device(case, {}) - ref).max() <= TOL
+    change = _prefill_mistakes(case)[mistake]
+    got = _prefill_device(case, change)
+    err = float(np.abs(got - ref).max())
+    print(f"prefill, {mistake}: max abs err against the correct oracle "
+          f"{err:.3f}")
+    assert err > 10 * TOL
+    assert np.abs(got - _prefill_oracle(case, change)).max() <= TOL
+
+
+# -- cascade step ---------------------------------------------------------------
+
+def test_claimed_prefix_one_block_too_long_reads_the_first_members_block(
+        gpu_lib):
+    """A group whose claimed shared prefix runs one block past the blocks
+    its members really share: the cascade step reads that block through the
+    first member's table for every member (what the claim means), so it
+    matches the oracle over tables in which each member's entry is the
+    first member's, and misses the correct oracle by more than 10x the
+    tolerance (short own contexts make one block a large share)."""
+    from paged_kv_cache_451_amd import _lib
+    cfg = CONFIG_BY_NAME["prefix_shared_bf16"].replace(
+        num_seqs=6, prefix_len=64, lo=20, hi=40)
+    case = build_case(cfg, 8)
+    p = 64 // 16
+    tab = case.block_tables.numpy()
+    assert all(tab[m, p] != tab[0, p] for m in range(1, 6))
+
+    def step(prefix_blocks):
+        dev = {k: getattr(case, k).cuda() for k in
+               ("q", "k_pool", "v_pool", "block_tables", "seq_lens",
+                "slot_mapping", "k_new", "v_new")}
+        out = torch.full_like(dev["q"], float("nan"))
+        _lib.pa_decode_append_shared(
+            dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
+            dev["seq_lens"], case.scale, out, dev["k_new"], dev["v_new"],
+            dev["slot_mapping"],
+            torch.tensor([0, 6], dtype=torch.int32, device="cuda"),
+            torch.tensor([prefix_blocks], dtype=torch.int32, device="cuda"),
+            max_seq_len=case.max_seq_len)
+        torch.cuda.synchronize()
+        g = out.cpu().to(torch.float64).numpy()
+        assert np.isfinite(g).all()
+        return g
+
+    ref = _oracle(case)
+    assert np.abs(step(p) - ref).max() <= TOL
+    got = step(p + 1)
+    err = float(np.abs(got - ref).max())
+    print(f"cascade, prefix claimed one block too long: max abs err "
+          f"against the correct oracle {err:.3f}")
+    assert err > 10 * TOL
+    claimed = tab.copy()
+    claimed[1:, p] = tab[0, p]
+    assert np.abs(got - _oracle(case, block_tables=claimed)).max() <= TOL
