@@ -538,6 +538,27 @@ def test_step_many_short_sequences(gpu_lib, spec, fused):
     assert err <= TOL[case.config.kv_dtype]
 
 
+@pytest.mark.parametrize("lens, kv_dtype", [([131072, 5], "bf16"),
+                                             ([262144, 40], "fp8_e4m3fn")])
+def test_one_very_long_sequence(gpu_lib, lens, kv_dtype):
+    """A context far longer than the workloads' (128 k tokens in bf16, 256 k
+    in fp8) next to a short one: the long sequence crosses every range of
+    its heads, so the merge folds about 128 partials per head.  Both step
+    forms, every output element, the pools byte for byte."""
+    case = _custom_case(lens, hq=32, hkv=8, d=128, kv_dtype=kv_dtype,
+                        seed=13)
+    ref = oracle_out(case)
+    out, dev = run_fused(case)
+    assert_pools_equal_oracle_append(case, dev)
+    err = max_err(out, ref)
+    out2, dev2 = run_step(gpu_lib, case)
+    assert_pools_equal_oracle_append(case, dev2)
+    err2 = max_err(out2, ref)
+    print(f"{lens[0]} tokens, {kv_dtype}: max abs err fused {err:.3e}, "
+          f"append + decode {err2:.3e}")
+    assert max(err, err2) <= TOL[kv_dtype]
+
+
 def test_fused_step_dominant_new_token(gpu_lib):
     """The newest token carries a large key along q: its weight is ~1 and
     the output is its V row, which only k_new / v_new hold before the call

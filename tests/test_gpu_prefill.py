@@ -344,3 +344,15 @@ def test_scores_that_keep_growing_along_the_keys(gpu_lib):
     out = run(case)
     ref = oracle.paged_prefill(**prefill_args(case))
     assert max_err(out, ref) <= TOL
+
+
+def test_chunks_after_a_very_long_context(gpu_lib):
+    """Chunks of 64 and 3 tokens after 131 000 cached tokens: one query
+    tile walks about 2 050 64-key steps, far more than the workload's."""
+    case = build_prefill_case(cfg(num_seqs=2, prior_lo=131000,
+                                  prior_hi=131000), seed=37, chunks=[64, 3])
+    out = run(case)
+    ref = oracle.paged_prefill(**prefill_args(case))
+    err = max_err(out, ref)
+    print(f"131000 cached tokens: max abs err {err:.3e}")
+    assert err <= TOL
