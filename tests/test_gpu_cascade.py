@@ -262,3 +262,16 @@ def test_dominant_key_probes_across_the_prefix_boundary(kv_dtype):
     for b, t, v in probes:
         err = (got[b] - v[g_of]).abs().max().item()
         assert err <= tol, (b, t, err)
+
+
+def test_very_long_shared_prefix():
+    """A 65 536-token prefix shared by 8 sequences: the shared-prefix pass
+    walks 1 024 64-key steps split over its key ranges."""
+    cfg = CONFIG_BY_NAME["prefix_shared_bf16"].replace(
+        num_seqs=8, prefix_len=65536, lo=1, hi=200)
+    case = build_case(cfg, 6)
+    out, dev = run_shared(case, [0, 8], [65536 // 16])
+    err = max_err(out, oracle_ref(case))
+    print(f"65536-token shared prefix: max abs err {err:.3e}")
+    assert err <= TOL
+    assert_pools_appended(case, dev)
