@@ -133,11 +133,20 @@ class FreeBlockQueue:
         return out
 
 
+_KEY_LAYOUT: Dict[int, struct.Struct] = {}
+
+
 def hash_block_tokens(parent_hash: int, token_ids: Sequence[int]) -> int:
-    """Key of a full block: its token ids chained to its parent's key."""
-    h = hashlib.sha256(struct.pack("<Q", parent_hash & (2**64 - 1)))
-    h.update(np.asarray(token_ids, dtype="<i8").tobytes())
-    return int.from_bytes(h.digest()[:8], "little")
+    """Key of a full block: its token ids chained to its parent's key (the
+    first 8 bytes of the SHA-256 of the parent key, as a little-endian
+    uint64, followed by the ids as little-endian int64)."""
+    n = len(token_ids)
+    layout = _KEY_LAYOUT.get(n)
+    if layout is None:
+        layout = _KEY_LAYOUT[n] = struct.Struct(f"<Q{n}q")
+    digest = hashlib.sha256(
+        layout.pack(parent_hash & (2**64 - 1), *token_ids)).digest()
+    return int.from_bytes(digest[:8], "little")
 
 
 class BlockPool:
