@@ -144,6 +144,11 @@ class Engine:
         self.last_out = None
         self.last_batch: List[int] = []
         self._dev_rand: Dict[str, object] = {}
+        # pinned staging buffers of the host-to-device uploads, used in
+        # turn, each with the event recorded after the copy that last read
+        # it, so that the host never waits for the device's queued work
+        self._staging: List[Optional[tuple]] = [None] * 3
+        self._staging_next = 0
         # (start event, end event, KV bytes) of each decode, when timed
         self.time_decode = False
         self.decode_events: List[tuple] = []
@@ -320,13 +325,39 @@ class Engine:
 
     def _upload(self, *arrays):
         """One host-to-device copy of several int32 arrays; returns their
-        device views in order, each starting on a 64-byte boundary."""
+        device views in order, each starting on a 64-byte boundary.  On a
+        GPU the copy is asynchronous, from a pinned staging buffer, so the
+        host goes on scheduling while the device works through the steps
+        already queued (a copy from pageable memory would wait for them)."""
+        torch = self.torch
         sizes = [a.size for a in arrays]
         offs = np.cumsum([0] + [-(-n // 16) * 16 for n in sizes])
-        flat = np.zeros(int(offs[-1]), dtype=np.int32)
-        for a, o in zip(arrays, offs):
-            flat[o:o + a.size] = a.ravel()
-        buf = self.torch.from_numpy(flat).to(self.device)
+        total = int(offs[-1])
+        if torch.device(self.device).type != "cuda":
+            flat = np.zeros(total, dtype=np.int32)
+            for a, o in zip(arrays, offs):
+                flat[o:o + a.size] = a.ravel()
+            buf = torch.from_numpy(flat).to(self.device)
+        else:
+            k = self._staging_next
+            self._staging_next = (k + 1) % len(self._staging)
+            held = self._staging[k]
+            if held is not None:
+                held[1].synchronize()     # its last copy has been read
+            if held is None or held[0].numel() < total:
+                host = torch.empty(max(total, 1 << 16), dtype=torch.int32,
+                                   pin_memory=True)
+            else:
+                host = held[0]
+            flat = host.numpy()
+            flat[:total] = 0
+            for a, o in zip(arrays, offs):
+                flat[o:o + a.size] = a.ravel()
+            buf = torch.empty(total, dtype=torch.int32, device=self.device)
+            buf.copy_(host[:total], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record()
+            self._staging[k] = (host, ev)
         return [buf[o:o + a.size].view(a.shape) for a, o in zip(arrays, offs)]
 
     def _prefill(self, n, host, dev_ints) -> None:
