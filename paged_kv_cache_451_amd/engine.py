@@ -199,6 +199,7 @@ class Engine:
     def _admit(self) -> List[tuple]:
         """FCFS admission; returns (request, cached prompt tokens) pairs."""
         admitted = []
+        need = self._growth_need()    # grows with each admission below
         while self.waiting:
             if self.max_running is not None and \
                     len(self.running) >= self.max_running:
@@ -221,7 +222,7 @@ class Engine:
             take = (self.mgr.blocks_to_admit(ids, keys) if self.prefix_caching
                     else self.mgr.blocks_needed(len(ids)))
             grow = 1 if len(ids) % BLOCK_SIZE == 0 else 0
-            if take + self._growth_need() + grow > self.pool.num_free:
+            if take + need + grow > self.pool.num_free:
                 break
             if self.prefix_caching:
                 # a prompt written over several steps registers its blocks
@@ -240,6 +241,7 @@ class Engine:
             if req.admitted_step < 0:
                 req.admitted_step = self.step_no
             admitted.append((req, hits * BLOCK_SIZE))
+            need += grow
         return admitted
 
     # -- device work -------------------------------------------------------------
