@@ -100,6 +100,10 @@ def parse():
                         "prefill, each chunk attended with pa_prefill); 0 "
                         "writes whole prompts on admission without prefill "
                         "attention (the default loop)")
+    p.add_argument("--block-manager", choices=["native", "python"],
+                   default="native",
+                   help="--op engine: the host block manager (native: "
+                        "libpa_host.so; python: pool.py; the same rules)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the bench, run three plain 1 GiB device "
                         "copies (the reference kernel that scales HBM "
@@ -596,7 +600,8 @@ def bench_engine(a, torch):
     chunked = a.prefill_budget > 0
     e = Engine(nb, 32, 8, 128, device="cuda:0", seed=a.seed or 0,
                max_prefill_tokens=a.prefill_budget if chunked else None,
-               prefill_attention=chunked)
+               prefill_attention=chunked,
+               native_pool=a.block_manager == "native")
     max_len = 0
     for i in range(1024):
         p = int(rng.integers(128, 2049))
@@ -641,7 +646,8 @@ def bench_engine(a, torch):
                    "prefill": (f"chunked, {a.prefill_budget} prompt tokens "
                                "per step, attended with pa_prefill"
                                if chunked else "whole prompts written on "
-                               "admission, not attended")},
+                               "admission, not attended"),
+                   "block_manager": a.block_manager},
         "prefill_tokens_per_s": round(
             sum(s.prefill_tokens for s in stats) / wall, 1),
         "mean_running": round(float(np.mean(batch)), 1),

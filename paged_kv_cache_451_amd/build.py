@@ -5,8 +5,10 @@
 Compiles every ``csrc/*.hip`` with hipcc for gfx950 into ``_build/`` and
 links ``paged_kv_cache_451_amd/libpa.so``; the benchmark's measurement probe
 (``csrc/probe/*.hip``, declared in ``include/pa_probe.h``) goes into
-``paged_kv_cache_451_amd/libpa_probe.so``.  Runs on a machine without a GPU
-(hipcc cross-compiles).
+``paged_kv_cache_451_amd/libpa_probe.so``; the native host block manager
+(``csrc/host/*.cpp``, declared in ``include/pa_host.h``) is built with the
+host C++ compiler into ``paged_kv_cache_451_amd/libpa_host.so``.  Runs on a
+machine without a GPU (hipcc cross-compiles).
 """
 from __future__ import annotations
 
@@ -24,6 +26,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
+HOST_LIB = os.path.join(PKG, "libpa_host.so")
+CXX = os.environ.get("CXX") or shutil.which("g++") or "g++"
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC") or shutil.which("hipcc") or \
@@ -67,11 +71,25 @@ def _link(srcs, lib, verbose):
     os.replace(tmp, lib)
 
 
+def _host_lib(verbose):
+    """The native host block manager (host code only, include/pa_host.h)."""
+    tmp = HOST_LIB + ".tmp"
+    cmd = [CXX, "-O2", "-std=c++17", "-shared", "-fPIC", "-Wall",
+           f"-I{INCLUDE}", *sorted(glob.glob(os.path.join(CSRC, "host",
+                                                          "*.cpp"))),
+           "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    _run(cmd)
+    os.replace(tmp, HOST_LIB)
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     _link(sorted(glob.glob(os.path.join(CSRC, "*.hip"))), LIB, verbose)
     _link(sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip"))), PROBE_LIB,
           verbose)
+    _host_lib(verbose)
     return LIB
 
 

@@ -71,10 +71,15 @@ class Request:
     # (token count, prefix-cache keys of its full blocks), computed once
     # for the tokens a waiting request is priced and admitted with
     keys: Optional[tuple] = field(default=None, repr=False, compare=False)
+    # prompt plus output tokens, kept up to date by add_output
+    num_tokens: int = field(default=0, init=False, compare=False)
 
-    @property
-    def num_tokens(self) -> int:
-        return len(self.prompt_ids) + len(self.output_ids)
+    def __post_init__(self):
+        self.num_tokens = len(self.prompt_ids) + len(self.output_ids)
+
+    def add_output(self, token: int) -> None:
+        self.output_ids.append(token)
+        self.num_tokens += 1
 
     @property
     def done(self) -> bool:
@@ -106,7 +111,10 @@ class Engine:
     """Continuous batching over a paged KV pool on one GPU.
 
     ``device=None`` runs the scheduler and block manager only (no kernels),
-    for host-side tests.  ``mirror=True`` records, for the last step, the
+    for host-side tests.  ``native_pool=True`` keeps the blocks in the
+    native block manager (``native_pool.py``, the same rules and keys in C++,
+    one library call per step for the decode's slots and tables) instead of
+    ``pool.py``'s; ``self.pool`` is then None.  ``mirror=True`` records, for the last step, the
     host copies of every K/V row written with its slots (``last_writes``,
     in the order the device writes them) and the step's queries, tables and
     lengths, so that a test can rebuild the pools and check each decode
@@ -118,13 +126,19 @@ class Engine:
                  max_running: Optional[int] = None,
                  prefix_caching: bool = True, mirror: bool = False,
                  max_prefill_tokens: Optional[int] = None,
-                 prefill_attention: bool = False):
+                 prefill_attention: bool = False, native_pool: bool = False):
         self.num_blocks = num_blocks
         self.hq, self.hkv, self.d = num_q_heads, num_kv_heads, head_size
         rng = np.random.default_rng(seed)
         self.rng = rng
-        self.pool = BlockPool(num_blocks, order=rng.permutation(num_blocks))
-        self.mgr = KVCacheManager(self.pool, BLOCK_SIZE)
+        order = rng.permutation(num_blocks)
+        if native_pool:
+            from .native_pool import NativeKVCacheManager
+            self.pool = None
+            self.mgr = NativeKVCacheManager(num_blocks, BLOCK_SIZE, order)
+        else:
+            self.pool = BlockPool(num_blocks, order=order)
+            self.mgr = KVCacheManager(self.pool, BLOCK_SIZE)
         self.max_running = max_running
         self.prefix_caching = prefix_caching
         if max_prefill_tokens is not None and max_prefill_tokens < 1:
@@ -183,15 +197,14 @@ class Engine:
 
     def _growth_need(self) -> int:
         """Blocks the running requests take for this step's new tokens."""
-        return sum(1 for r in self.running
-                   if self.mgr.req_to_blocks[r.req_id].num_tokens %
-                   BLOCK_SIZE == 0)
+        # a running request's stored tokens are its prompt and outputs
+        return sum(1 for r in self.running if r.num_tokens % BLOCK_SIZE == 0)
 
     def _ensure_growth(self) -> int:
         """Every running request needs a slot for its next token; preempt
         from the back until the blocks needed fit in the pool."""
         preempted = 0
-        while self.running and self._growth_need() > self.pool.num_free:
+        while self.running and self._growth_need() > self.mgr.num_free:
             self._preempt_last()
             preempted += 1
         return preempted
@@ -222,7 +235,7 @@ class Engine:
             take = (self.mgr.blocks_to_admit(ids, keys) if self.prefix_caching
                     else self.mgr.blocks_needed(len(ids)))
             grow = 1 if len(ids) % BLOCK_SIZE == 0 else 0
-            if take + need + grow > self.pool.num_free:
+            if take + need + grow > self.mgr.num_free:
                 break
             if self.prefix_caching:
                 # a prompt written over several steps registers its blocks
@@ -400,14 +413,15 @@ class Engine:
         finished = 0
         if batch:
             tokens = self.rng.integers(1 << 17, size=len(batch)).tolist()
-            slots = [self.mgr.append_slot(r.req_id, token_id=t)
-                     for r, t in zip(batch, tokens)]
+            slots = self.mgr.append_slots([r.req_id for r in batch], tokens)
             copies = self.mgr.take_copies()
             assert not copies, "running requests never share a partial block"
             self._decode(batch, slots)
-            for r, s in zip(batch, slots):
-                tok = self.mgr.req_to_blocks[r.req_id].token_ids
-                r.output_ids.append(tok[-1] if tok else 0)
+            # the sampled token (kept as the request's output when the
+            # manager keeps token ids, for the prefix cache)
+            keep = self.prefix_caching
+            for r, t in zip(batch, tokens):
+                r.add_output(t if keep else 0)
                 r.written += 1
             still = []
             for r in self.running:
@@ -424,9 +438,8 @@ class Engine:
             admitted=len(admitted), preempted=preempted, finished=finished,
             prefill_tokens=prefill, prefill_chunks=len(chunks),
             cached_prefix_tokens=cached,
-            blocks_used=self.num_blocks - self.pool.num_free,
-            slots_used=sum(self.mgr.req_to_blocks[r.req_id].num_tokens
-                           for r in self.running))
+            blocks_used=self.num_blocks - self.mgr.num_free,
+            slots_used=sum(r.num_tokens for r in self.running))
         self.step_no += 1
         return st
 

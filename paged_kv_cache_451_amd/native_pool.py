@@ -1,0 +1,235 @@
+"""ctypes binding of the native host block manager (``libpa_host.so``,
+``include/pa_host.h``).
+
+``NativeKVCacheManager`` keeps the rules and the block keys of
+``pool.KVCacheManager`` (free-block queue, reference counts, hash-keyed
+prefix cache, copy-on-write, allocate-on-growth) with the methods the
+engine's step uses, plus batched forms (``append_slots``, ``tables``) that
+cost one library call per step instead of one Python call per request.
+Argument marshalling only; the library must be built (``build.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libpa_host.so")
+_lib = None
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_SIGS = {
+    "pa_bm_create": (_p, [_i32, _i32, _p]),
+    "pa_bm_destroy": (None, [_p]),
+    "pa_bm_num_free": (_i32, [_p]),
+    "pa_bm_num_cached": (_i32, [_p]),
+    "pa_bm_prefix_keys": (None, [_p, _i32, _i32, _p]),
+    "pa_bm_blocks_to_admit": (_i32, [_p, _i32, _p, _i32]),
+    "pa_bm_admit": (_i32, [_p, _i64, _i32]),
+    "pa_bm_admit_cached": (_i32, [_p, _i64, _p, _i32, _p, _i32, _i32]),
+    "pa_bm_cache_written": (_i32, [_p, _i64, _i32]),
+    "pa_bm_append_slots": (_i32, [_p, _p, _p, _i32, _p]),
+    "pa_bm_num_copies": (_i32, [_p]),
+    "pa_bm_take_copies": (_i32, [_p, _p, _p]),
+    "pa_bm_free_seq": (_i32, [_p, _i64]),
+    "pa_bm_num_tokens": (_i32, [_p, _i64]),
+    "pa_bm_num_blocks_of": (_i32, [_p, _i64]),
+    "pa_bm_block_ids": (_i32, [_p, _i64, _p]),
+    "pa_bm_max_blocks": (_i32, [_p, _p, _i32]),
+    "pa_bm_tables": (_i32, [_p, _p, _i32, _i32, _i32, _p, _p]),
+    "pa_bm_ref_count": (_i32, [_p, _i32]),
+    "pa_bm_free_queue": (_i32, [_p, _p]),
+}
+
+
+def load():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m paged_kv_cache_451_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _tokens(token_ids) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(token_ids, dtype=np.int64))
+
+
+def prefix_keys(token_ids: Sequence[int], block_size: int = 16) -> np.ndarray:
+    """Keys of the full blocks of ``token_ids`` (uint64), the same values as
+    ``pool.KVCacheManager.prefix_keys``."""
+    toks = _tokens(token_ids)
+    out = np.zeros(len(toks) // block_size, dtype=np.uint64)
+    if len(out):
+        load().pa_bm_prefix_keys(_ptr(toks), len(toks), block_size,
+                                 _ptr(out))
+    return out
+
+
+def _check(status: int, what: str) -> int:
+    if status == -3:
+        raise MemoryError(f"{what}: KV block pool exhausted")
+    if status == -2:
+        raise KeyError(f"{what}: unknown or already admitted sequence")
+    if status < 0:
+        raise ValueError(f"{what}: invalid argument ({status})")
+    return status
+
+
+class NativeKVCacheManager:
+    """The block manager of ``pool.KVCacheManager`` over a pool of
+    ``num_blocks`` blocks, in native code.  ``order`` is the initial
+    free-queue order (a permutation of the block ids)."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16,
+                 order: Optional[Sequence[int]] = None):
+        lib = load()
+        self._lib = lib
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        ordr = None
+        if order is not None:
+            ordr = np.ascontiguousarray(np.asarray(order, dtype=np.int32))
+            if ordr.shape != (num_blocks,):
+                raise ValueError("order must hold num_blocks block ids")
+        h = lib.pa_bm_create(num_blocks, block_size,
+                             None if ordr is None else _ptr(ordr))
+        if not h:
+            raise ValueError("invalid pool size, block size or order")
+        self._h = h
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._lib.pa_bm_destroy(h)
+
+    # -- pool state ------------------------------------------------------------
+    @property
+    def num_free(self) -> int:
+        return self._lib.pa_bm_num_free(self._h)
+
+    @property
+    def num_cached(self) -> int:
+        return self._lib.pa_bm_num_cached(self._h)
+
+    def ref_count(self, block: int) -> int:
+        return self._lib.pa_bm_ref_count(self._h, block)
+
+    def free_queue(self) -> List[int]:
+        out = np.zeros(max(self.num_free, 1), dtype=np.int32)
+        n = self._lib.pa_bm_free_queue(self._h, _ptr(out))
+        return out[:n].tolist()
+
+    # -- admission -------------------------------------------------------------
+    def blocks_needed(self, num_tokens: int) -> int:
+        return -(-num_tokens // self.block_size)
+
+    def prefix_keys(self, token_ids: Sequence[int]) -> np.ndarray:
+        return prefix_keys(token_ids, self.block_size)
+
+    def _keys(self, token_ids, keys) -> np.ndarray:
+        k = self.prefix_keys(token_ids) if keys is None else \
+            np.ascontiguousarray(np.asarray(keys, dtype=np.uint64))
+        if len(k) != len(token_ids) // self.block_size:
+            raise ValueError("keys do not match the tokens' full blocks")
+        return k
+
+    def blocks_to_admit(self, token_ids: Sequence[int], keys=None) -> int:
+        k = self._keys(token_ids, keys)
+        return _check(self._lib.pa_bm_blocks_to_admit(
+            self._h, len(token_ids), _ptr(k), len(k)), "blocks_to_admit")
+
+    def admit(self, seq_id: int, num_tokens: int) -> bool:
+        return bool(_check(self._lib.pa_bm_admit(self._h, seq_id,
+                                                 num_tokens), "admit"))
+
+    def admit_cached(self, seq_id: int, token_ids: Sequence[int],
+                     register: bool = True, keys=None) -> Tuple[bool, int]:
+        toks = _tokens(token_ids)
+        k = self._keys(toks, keys)
+        r = self._lib.pa_bm_admit_cached(self._h, seq_id, _ptr(toks),
+                                         len(toks), _ptr(k), len(k),
+                                         int(register))
+        if r == -3:
+            return False, 0
+        return True, _check(r, "admit_cached")
+
+    def cache_written(self, seq_id: int, num_tokens: int) -> None:
+        _check(self._lib.pa_bm_cache_written(self._h, seq_id, num_tokens),
+               "cache_written")
+
+    # -- growth ----------------------------------------------------------------
+    def append_slots(self, seq_ids: Sequence[int],
+                     token_ids: Optional[Sequence[int]] = None) -> np.ndarray:
+        """One new token for each sequence, in order: their int32 slots."""
+        seqs = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        toks = None if token_ids is None else _tokens(token_ids)
+        if toks is not None and toks.shape != seqs.shape:
+            raise ValueError("one token id per sequence")
+        slots = np.zeros(len(seqs), dtype=np.int32)
+        _check(self._lib.pa_bm_append_slots(
+            self._h, _ptr(seqs), None if toks is None else _ptr(toks),
+            len(seqs), _ptr(slots)), "append_slots")
+        return slots
+
+    def append_slot(self, seq_id: int, token_id: Optional[int] = None) -> int:
+        return int(self.append_slots(
+            [seq_id], None if token_id is None else [token_id])[0])
+
+    def take_copies(self) -> List[Tuple[int, int]]:
+        n = self._lib.pa_bm_num_copies(self._h)
+        if n == 0:
+            return []
+        src = np.zeros(n, dtype=np.int32)
+        dst = np.zeros(n, dtype=np.int32)
+        self._lib.pa_bm_take_copies(self._h, _ptr(src), _ptr(dst))
+        return list(zip(src.tolist(), dst.tolist()))
+
+    def free_seq(self, seq_id: int) -> None:
+        _check(self._lib.pa_bm_free_seq(self._h, seq_id), "free_seq")
+
+    # -- views -----------------------------------------------------------------
+    def num_tokens(self, seq_id: int) -> int:
+        return _check(self._lib.pa_bm_num_tokens(self._h, seq_id),
+                      "num_tokens")
+
+    def block_ids(self, seq_id: int) -> List[int]:
+        n = _check(self._lib.pa_bm_num_blocks_of(self._h, seq_id),
+                   "block_ids")
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        self._lib.pa_bm_block_ids(self._h, seq_id, _ptr(out))
+        return out[:n].tolist()
+
+    def tables(self, seq_ids: Sequence[int], pad: int = -1,
+               width: Optional[int] = None):
+        """int32 ``block_tables`` [B, width] (padded with ``pad``) and
+        ``seq_lens`` [B] for ``seq_ids`` in that order."""
+        seqs = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        w = _check(self._lib.pa_bm_max_blocks(self._h, _ptr(seqs),
+                                              len(seqs)), "tables")
+        if width is not None:
+            if w > width:
+                raise ValueError("table width too small")
+            w = width
+        w = max(w, 1)
+        table = np.empty((len(seqs), w), dtype=np.int32)
+        lens = np.empty(len(seqs), dtype=np.int32)
+        _check(self._lib.pa_bm_tables(self._h, _ptr(seqs), len(seqs), w, pad,
+                                      _ptr(table), _ptr(lens)), "tables")
+        return table, lens

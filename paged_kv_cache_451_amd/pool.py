@@ -239,6 +239,10 @@ class KVCacheManager:
         # next append (copy-on-write); drained by take_copies()
         self.pending_copies: List[Tuple[int, int]] = []
 
+    @property
+    def num_free(self) -> int:
+        return self.pool.num_free
+
     # -- admission -----------------------------------------------------------
     def blocks_needed(self, num_tokens: int) -> int:
         return -(-num_tokens // self.block_size)
@@ -429,12 +433,24 @@ class KVCacheManager:
                         parent, st.token_ids[idx * bs:(idx + 1) * bs]))
         return slot
 
+    def append_slots(self, seq_ids: Sequence[int],
+                     token_ids: Optional[Sequence[int]] = None) -> np.ndarray:
+        """``append_slot`` for each sequence in order: their int32 slots."""
+        if token_ids is None:
+            token_ids = [None] * len(seq_ids)
+        return np.asarray([self.append_slot(s, t)
+                           for s, t in zip(seq_ids, token_ids)],
+                          dtype=np.int32)
+
     def free_seq(self, seq_id: int) -> None:
         st = self.req_to_blocks.pop(seq_id)
         for blk in st.blocks:
             self.pool.free(blk)
 
     # -- views ---------------------------------------------------------------
+    def num_tokens(self, seq_id: int) -> int:
+        return self.req_to_blocks[seq_id].num_tokens
+
     def block_ids(self, seq_id: int) -> List[int]:
         return [b.block_id for b in self.req_to_blocks[seq_id].blocks]
 

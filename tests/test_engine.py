@@ -318,3 +318,40 @@ def test_one_upload_carries_every_int_array_of_a_step():
     for t in (ta, tb, td):
         assert t.is_contiguous() and t.dtype == torch.int32
         assert (t.data_ptr() - ta.data_ptr()) % 64 == 0
+
+
+@pytest.mark.parametrize("budget", [None, 37])
+def test_native_block_manager_runs_the_same_loop(budget):
+    """The engine on the native block manager takes the same steps as on
+    the Python one: equal statistics every step, and equal K/V slots,
+    block tables and lengths for every write and decode (preemptions and
+    prefix-cache hits included)."""
+    rng = np.random.default_rng(31)
+    system = rng.integers(0, 1000, size=64).tolist()
+    reqs = [(i, (system if i % 3 else []) + rng.integers(
+        0, 1000, size=int(rng.integers(5, 150))).tolist(),
+        int(rng.integers(3, 40))) for i in range(30)]
+    engines = [Engine(60, 8, 2, 64, seed=8, mirror=True,
+                      max_prefill_tokens=budget, native_pool=n)
+               for n in (False, True)]
+    for e in engines:
+        for i, p, o in reqs:
+            e.add_request(Request(i, list(p), o))
+    pre = hits = steps = 0
+    while any(e.has_work() for e in engines):
+        a, b = (e.step() for e in engines)
+        assert a == b
+        wa, wb = (e.last_writes for e in engines)
+        assert len(wa) == len(wb)
+        for x, y in zip(wa, wb):
+            assert np.array_equal(x[2], y[2])
+        if a.running:
+            for f in ("last_tables", "last_lens"):
+                assert np.array_equal(getattr(engines[0], f),
+                                      getattr(engines[1], f))
+        pre += a.preempted
+        hits += a.cached_prefix_tokens
+        steps += 1
+        assert steps < 20_000
+    assert pre > 0 and hits > 0
+    assert engines[1].mgr.num_free == 60
