@@ -44,7 +44,8 @@ typedef struct pa_bm pa_bm;
 
 /* num_blocks blocks of block_size token slots; order: the initial free-queue
  * order, a permutation of 0..num_blocks-1 (NULL = ascending).  NULL on a bad
- * argument or an order that is not a permutation. */
+ * argument (num_blocks * block_size must fit in int32, as slot ids do) or
+ * an order that is not a permutation. */
 pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size,
                     const int32_t* order);
 void pa_bm_destroy(pa_bm* bm);

@@ -7,6 +7,7 @@
 #include "pa_host.h"
 
 #include <cstddef>
+#include <cstdint>
 #include <cstring>
 #include <new>
 #include <unordered_map>
@@ -189,7 +190,9 @@ struct pa_bm {
       hit_buf.push_back(it->second);
     }
   }
-  int32_t needed(int32_t n) const { return (n + bs - 1) / bs; }
+  int32_t needed(int32_t n) const {
+    return (int32_t)(((int64_t)n + bs - 1) / bs);
+  }
   const uint64_t* keys_for(const int64_t* tokens, int32_t n,
                            const uint64_t* keys) {
     if (keys) return keys;
@@ -203,7 +206,9 @@ extern "C" {
 
 pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size,
                     const int32_t* order) {
-  if (num_blocks <= 0 || block_size <= 0 || num_blocks > (1 << 30))
+  // slots are int32: every slot id block * block_size + offset must fit
+  if (num_blocks <= 0 || block_size <= 0 ||
+      (int64_t)num_blocks * block_size > INT32_MAX)
     return nullptr;
   pa_bm* bm = new (std::nothrow) pa_bm();
   if (!bm) return nullptr;

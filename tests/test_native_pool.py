@@ -183,6 +183,8 @@ def test_errors_are_reported():
         nat.append_slots([1])
     with pytest.raises(ValueError):
         native_pool.NativeKVCacheManager(4, 16, [0, 1, 1, 2])
+    with pytest.raises(ValueError):                # slots would overflow
+        native_pool.NativeKVCacheManager(1 << 27, 16)
     with pytest.raises(ValueError):
         nat.blocks_to_admit(list(range(32)), keys=[1])
 
