@@ -427,8 +427,10 @@ int32_t pa_bm_block_ids(const pa_bm* bm, int64_t seq, int32_t* ids_out) {
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return -2;
   const std::vector<int32_t>& b = it->second.blocks;
-  if (!b.empty() && !ids_out) return -1;
-  std::memcpy(ids_out, b.data(), b.size() * sizeof(int32_t));
+  if (!b.empty()) {
+    if (!ids_out) return -1;
+    std::memcpy(ids_out, b.data(), b.size() * sizeof(int32_t));
+  }
   return (int32_t)b.size();
 }
 
@@ -457,7 +459,7 @@ int32_t pa_bm_tables(const pa_bm* bm, const int64_t* seqs, int32_t count,
     const std::vector<int32_t>& b = it->second.blocks;
     if ((int32_t)b.size() > width) return -1;
     int32_t* row = table_out + (size_t)i * width;
-    std::memcpy(row, b.data(), b.size() * sizeof(int32_t));
+    if (!b.empty()) std::memcpy(row, b.data(), b.size() * sizeof(int32_t));
     for (int32_t j = (int32_t)b.size(); j < width; ++j) row[j] = pad;
     lens_out[i] = it->second.num_tokens;
   }
