@@ -150,6 +150,8 @@ class Engine:
         self.last_prefill = None
         self.waiting: Deque[Request] = deque()
         self.running: List[Request] = []        # in admission order
+        # running requests whose prompt is not all written, in order
+        self._prefilling: List[Request] = []
         self.finished: List[Request] = []
         self.step_no = 0
         self.device = device
@@ -190,6 +192,9 @@ class Engine:
     # -- scheduling ------------------------------------------------------------
     def _preempt_last(self) -> Request:
         victim = self.running.pop()
+        # the prompts being written are a subsequence of the running list
+        if self._prefilling and self._prefilling[-1] is victim:
+            self._prefilling.pop()
         self.mgr.free_seq(victim.req_id)
         victim.preemptions += 1
         self.waiting.appendleft(victim)
@@ -200,19 +205,22 @@ class Engine:
         # a running request's stored tokens are its prompt and outputs
         return sum(1 for r in self.running if r.num_tokens % BLOCK_SIZE == 0)
 
-    def _ensure_growth(self) -> int:
+    def _ensure_growth(self) -> tuple:
         """Every running request needs a slot for its next token; preempt
-        from the back until the blocks needed fit in the pool."""
+        from the back until the blocks needed fit in the pool.  Returns the
+        preemptions and the blocks the remaining requests need."""
         preempted = 0
-        while self.running and self._growth_need() > self.mgr.num_free:
+        need = self._growth_need()
+        while self.running and need > self.mgr.num_free:
             self._preempt_last()
             preempted += 1
-        return preempted
+            need = self._growth_need()
+        return preempted, need
 
-    def _admit(self) -> List[tuple]:
-        """FCFS admission; returns (request, cached prompt tokens) pairs."""
+    def _admit(self, need: int) -> List[tuple]:
+        """FCFS admission next to the running requests' growth ``need``;
+        returns (request, cached prompt tokens) pairs."""
         admitted = []
-        need = self._growth_need()    # grows with each admission below
         while self.waiting:
             if self.max_running is not None and \
                     len(self.running) >= self.max_running:
@@ -251,6 +259,8 @@ class Engine:
             self.running.append(req)
             self.waiting.popleft()
             req.written = hits * BLOCK_SIZE
+            if req.written < req.num_tokens:
+                self._prefilling.append(req)
             if req.admitted_step < 0:
                 req.admitted_step = self.step_no
             admitted.append((req, hits * BLOCK_SIZE))
@@ -288,9 +298,7 @@ class Engine:
         admission order, within the prompt-token budget."""
         budget = self.max_prefill_tokens
         chunks = []
-        for r in self.running:
-            if r.written >= r.num_tokens:
-                continue
+        for r in self._prefilling:
             n = r.num_tokens - r.written
             if budget is not None:
                 if budget == 0:
@@ -303,21 +311,22 @@ class Engine:
     def _write_prompts(self, chunks) -> int:
         """Writes the chunks' K/V (one append) and, with prefill attention,
         attends each chunk's tokens to everything stored before them."""
-        slots = []
+        parts = []
         for req, lo, hi in chunks:
-            blocks = self.mgr.block_ids(req.req_id)
-            slots += [blocks[t // BLOCK_SIZE] * BLOCK_SIZE + t % BLOCK_SIZE
-                      for t in range(lo, hi)]
+            blocks = np.asarray(self.mgr.block_ids(req.req_id), dtype=np.int64)
+            t = np.arange(lo, hi)
+            parts.append(blocks[t // BLOCK_SIZE] * BLOCK_SIZE + t % BLOCK_SIZE)
         for req, lo, hi in chunks:
             req.written = hi
             if self.prefix_caching and self.max_prefill_tokens is not None:
                 self.mgr.cache_written(req.req_id, hi)
-        if not slots:
+        n = sum(len(x) for x in parts)
+        if n == 0:
             return 0
         if self.device is None and not self.mirror:
-            return len(slots)
-        k, v = self._random_rows(len(slots))
-        slots_np = np.asarray(slots, dtype=np.int32)
+            return n
+        k, v = self._random_rows(n)
+        slots_np = np.concatenate(parts).astype(np.int32)
         if self.mirror:
             self._record_write(k, v, slots_np)
         if self.device is not None:
@@ -335,8 +344,8 @@ class Engine:
             _lib.pa_kv_append(k.to(self.device), v.to(self.device),
                               dev_ints[0], self.k_pool, self.v_pool)
             if self.prefill_attention:
-                self._prefill(len(slots), ints[1:], dev_ints[1:])
-        return len(slots)
+                self._prefill(n, ints[1:], dev_ints[1:])
+        return n
 
     def _upload(self, *arrays):
         """One host-to-device copy of several int32 arrays; returns their
@@ -398,8 +407,8 @@ class Engine:
     def step(self) -> StepStats:
         self.last_writes = []
         self.last_prefill = None
-        preempted = self._ensure_growth()
-        admitted = self._admit()
+        preempted, need = self._ensure_growth()
+        admitted = self._admit(need)
         if not self.running and self.waiting:
             req = self.waiting[0]
             raise MemoryError(
@@ -407,9 +416,13 @@ class Engine:
                 f"in an empty pool of {self.num_blocks} blocks")
         chunks = self._prefill_chunks()
         prefill = self._write_prompts(chunks)
+        if chunks:
+            self._prefilling = [r for r in self._prefilling
+                                if r.written < r.num_tokens]
         cached = sum(c for _, c in admitted)
         # requests whose tokens are all stored decode this step
-        batch = [r for r in self.running if r.written >= r.num_tokens]
+        batch = [r for r in self.running if r.written >= r.num_tokens] \
+            if self._prefilling else list(self.running)
         finished = 0
         if batch:
             tokens = self.rng.integers(1 << 17, size=len(batch)).tolist()
@@ -423,16 +436,16 @@ class Engine:
             for r, t in zip(batch, tokens):
                 r.add_output(t if keep else 0)
                 r.written += 1
-            still = []
-            for r in self.running:
-                if r.done:
-                    self.mgr.free_seq(r.req_id)
-                    r.finished_step = self.step_no
-                    self.finished.append(r)
-                    finished += 1
-                else:
-                    still.append(r)
-            self.running = still
+            # only requests that decoded can finish; they leave in running
+            # order (the order their blocks return to the free queue)
+            done = [r for r in batch if r.done]
+            for r in done:
+                self.mgr.free_seq(r.req_id)
+                r.finished_step = self.step_no
+                self.finished.append(r)
+            finished = len(done)
+            if done:
+                self.running = [r for r in self.running if not r.done]
         st = StepStats(
             step=self.step_no, running=len(batch), waiting=len(self.waiting),
             admitted=len(admitted), preempted=preempted, finished=finished,
