@@ -433,12 +433,15 @@ class Engine:
             # the sampled token (kept as the request's output when the
             # manager keeps token ids, for the prefix cache)
             keep = self.prefix_caching
+            done = []
             for r, t in zip(batch, tokens):
-                r.add_output(t if keep else 0)
+                r.output_ids.append(t if keep else 0)
+                r.num_tokens += 1
                 r.written += 1
+                if len(r.output_ids) >= r.max_new_tokens:
+                    done.append(r)
             # only requests that decoded can finish; they leave in running
             # order (the order their blocks return to the free queue)
-            done = [r for r in batch if r.done]
             for r in done:
                 self.mgr.free_seq(r.req_id)
                 r.finished_step = self.step_no
