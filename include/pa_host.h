@@ -77,6 +77,11 @@ int32_t pa_bm_admit_cached(pa_bm* bm, int64_t seq, const int64_t* tokens,
                            int32_t n, const uint64_t* keys, int32_t n_keys,
                            int32_t register_now);
 
+/* A new sequence dst continuing src's context (parallel sampling, beam
+ * search): it shares every block of src (each touched), its length and its
+ * token ids; the first append into a shared partial block copies it. */
+int32_t pa_bm_fork(pa_bm* bm, int64_t src, int64_t dst);
+
 /* Registers seq's pending full blocks that lie within its first n tokens. */
 int32_t pa_bm_cache_written(pa_bm* bm, int64_t seq, int32_t n);
 

@@ -319,6 +319,20 @@ int32_t pa_bm_admit_cached(pa_bm* bm, int64_t seq, const int64_t* tokens,
   return nhit;
 }
 
+int32_t pa_bm_fork(pa_bm* bm, int64_t src, int64_t dst) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(src);
+  if (it == bm->seqs.end() || bm->seqs.count(dst)) return -2;
+  Seq s;
+  s.num_tokens = it->second.num_tokens;
+  s.blocks = it->second.blocks;
+  s.has_tokens = it->second.has_tokens;
+  s.tokens = it->second.tokens;
+  for (int32_t b : s.blocks) bm->touch(b);
+  bm->seqs.emplace(dst, std::move(s));
+  return 0;
+}
+
 int32_t pa_bm_cache_written(pa_bm* bm, int64_t seq, int32_t n) {
   if (!bm) return -1;
   auto it = bm->seqs.find(seq);

@@ -32,6 +32,7 @@ _SIGS = {
     "pa_bm_blocks_to_admit": (_i32, [_p, _i32, _p, _i32]),
     "pa_bm_admit": (_i32, [_p, _i64, _i32]),
     "pa_bm_admit_cached": (_i32, [_p, _i64, _p, _i32, _p, _i32, _i32]),
+    "pa_bm_fork": (_i32, [_p, _i64, _i64]),
     "pa_bm_cache_written": (_i32, [_p, _i64, _i32]),
     "pa_bm_append_slots": (_i32, [_p, _p, _p, _i32, _p]),
     "pa_bm_num_copies": (_i32, [_p]),
@@ -169,6 +170,11 @@ class NativeKVCacheManager:
         if r == -3:
             return False, 0
         return True, _check(r, "admit_cached")
+
+    def fork(self, src_id: int, new_id: int) -> None:
+        """A new sequence continuing src's context: it shares every block;
+        divergence is copy-on-write."""
+        _check(self._lib.pa_bm_fork(self._h, src_id, new_id), "fork")
 
     def cache_written(self, seq_id: int, num_tokens: int) -> None:
         _check(self._lib.pa_bm_cache_written(self._h, seq_id, num_tokens),

@@ -8,9 +8,9 @@ slots, copy pairs), the free queue in order, every block's reference count,
 the number of cached keys and the block tables of every live sequence.  The
 block keys are compared with the Python manager's SHA-256 keys over block
 sizes that put the hashed message on every side of SHA-256's 64-byte block
-and padding boundaries.  (The native manager has no fork or shared-prefix
-admission, the only sources of a shared partial block, so its copy-on-write
-branch is not reached here; the engine uses neither.)
+and padding boundaries.  The walks fork sequences too, so appends into
+shared partial blocks take the copy-on-write branch (the native manager has
+no admission with an explicit shared prefix; the engine uses neither).
 """
 import numpy as np
 import pytest
@@ -68,7 +68,7 @@ def _walk(seed, steps, num_blocks):
     prompts = [rng.integers(0, 1000, 90).tolist() for _ in range(3)]
     for _ in range(steps):
         op = rng.choice(["admit", "admit_cached", "append", "append",
-                         "append", "free", "written"])
+                         "append", "free", "written", "fork"])
         if op == "admit":
             n = int(rng.integers(0, 70))
             a, b = py.admit(next_id, n), nat.admit(next_id, n)
@@ -95,6 +95,12 @@ def _walk(seed, steps, num_blocks):
                 seen["deferred"] += not register
             else:
                 seen["refused"] += 1
+            next_id += 1
+        elif op == "fork" and live:
+            s = int(rng.choice(sorted(live)))
+            py.fork(s, next_id)
+            nat.fork(s, next_id)
+            live.add(next_id)
             next_id += 1
         elif op == "written" and cached_seqs:
             s = int(rng.choice(sorted(cached_seqs)))
@@ -142,6 +148,7 @@ def test_random_walk_matches_the_python_manager(seed):
     seen = _walk(seed, steps=1500, num_blocks=40)
     assert seen["hits"] > 0 and seen["refused"] > 0
     assert seen["deferred"] > 0 and seen["exhausted"] > 0
+    assert seen["copies"] > 0
 
 
 def test_shared_full_blocks_and_appended_keys_match_the_python_manager():
