@@ -237,6 +237,10 @@ def _probe_lib():
         lib.pa_probe_read_stream.argtypes = [vp, ctypes.c_size_t, vp,
                                              ctypes.c_int, vp]
         lib.pa_probe_read_stream.restype = ctypes.c_int
+        ci = ctypes.c_int
+        lib.pa_probe_scatter_v_store.argtypes = [vp, vp, ci, ci, ci, ci, ci,
+                                                 vp]
+        lib.pa_probe_scatter_v_store.restype = ctypes.c_int
         _PROBE = lib
     return _PROBE
 
@@ -365,6 +369,33 @@ def bench_append(a, torch, _lib):
     nbytes = a.tokens * hkv * d * 2 * (2 + out_bytes) + 4 * a.tokens
     gbs = nbytes / (avg * 1e-3) / 1e9
 
+    # the same launch's V stores alone (libpa_probe.so), on the same slots
+    # and pool: what the store pattern costs by itself
+    import ctypes
+    plib = _probe_lib()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def v_stores():
+        st = plib.pa_probe_scatter_v_store(
+            ctypes.c_void_p(vp.data_ptr()), ctypes.c_void_p(sl.data_ptr()),
+            a.tokens, hkv, d, nb, 1 if quant else 2, sp)
+        if st != 0:
+            raise RuntimeError(f"pa_probe_scatter_v_store failed ({st})")
+
+    for _ in range(a.warmup):
+        v_stores()
+    ev = _kernel_events(torch, a.steps)
+    for e0, e1 in ev:
+        e0.record()
+        v_stores()
+        e1.record()
+    torch.cuda.synchronize()
+    v_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+    pattern = {"kind": "the launch's V element stores alone, same slots "
+                       "(libpa_probe.so)",
+               "ms": round(v_ms, 5),
+               "share_of_append": round(v_ms / avg, 4)}
+
     cpu = None
     if not a.no_cpu_baseline:
         import oracle
@@ -406,7 +437,8 @@ def bench_append(a, torch, _lib):
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": nbytes,
                      "kernel_ms_avg": round(avg, 5),
-                     "kernel_ms_median": round(ms[len(ms) // 2], 5)},
+                     "kernel_ms_median": round(ms[len(ms) // 2], 5),
+                     "v_store_pattern": pattern},
         "cpu_baseline": cpu,
     }), flush=True)
 
