@@ -133,7 +133,7 @@ struct pa_bm {
   std::vector<int32_t> copy_src, copy_dst;
   std::vector<uint8_t> scratch;        // key input bytes
   std::vector<uint64_t> key_buf;
-  std::vector<int32_t> hit_buf;
+  mutable std::vector<int32_t> hit_buf;  // scratch of hits_of
 
   int32_t head() const { return nb; }
   int32_t tail() const { return nb + 1; }
@@ -182,7 +182,7 @@ struct pa_bm {
     }
   }
   // Cached blocks of the longest cached prefix (lookups stop at a miss).
-  void hits_of(const uint64_t* keys, int32_t n_keys) {
+  void hits_of(const uint64_t* keys, int32_t n_keys) const {
     hit_buf.clear();
     for (int32_t i = 0; i < n_keys; ++i) {
       auto it = cache.find(keys[i]);
@@ -256,9 +256,8 @@ void pa_bm_prefix_keys(const int64_t* tokens, int32_t n, int32_t block_size,
   }
 }
 
-int32_t pa_bm_blocks_to_admit(const pa_bm* cbm, int32_t n,
+int32_t pa_bm_blocks_to_admit(const pa_bm* bm, int32_t n,
                               const uint64_t* keys, int32_t n_keys) {
-  pa_bm* bm = const_cast<pa_bm*>(cbm);  // hit_buf is scratch only
   if (!bm || n < 0 || n_keys != n / bm->bs || (n_keys && !keys)) return -1;
   bm->hits_of(keys, n_keys);
   int32_t take = bm->needed(n) - (int32_t)bm->hit_buf.size();
