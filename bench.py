@@ -658,6 +658,8 @@ def bench_engine(a, torch):
         e.step()
     torch.cuda.synchronize()
     dec_ms = [e0.elapsed_time(e1) for e0, e1, _ in e.decode_events]
+    pf_ms = [e0.elapsed_time(e1) for e0, e1, _ in e.prefill_events]
+    pf_flops = [f for _, _, f in e.prefill_events]
     dec_bytes = [b for _, _, b in e.decode_events]
     dec_gbs = sum(dec_bytes) / (sum(dec_ms) * 1e-3) / 1e9
     tokens = sum(s.running for s in stats)
@@ -689,6 +691,11 @@ def bench_engine(a, torch):
         "preemptions": int(sum(s.preempted for s in stats)),
         "finished": len(e.finished),
         "decode_device_ms_per_step": round(float(np.mean(dec_ms)), 4),
+        "prefill_attention": (None if not pf_ms else {
+            "device_ms_per_launch": round(float(np.mean(pf_ms)), 4),
+            "tflops": round(sum(pf_flops) / (sum(pf_ms) * 1e-3) / 1e12, 2),
+            "frac_of_bf16_mfma_peak": round(
+                sum(pf_flops) / (sum(pf_ms) * 1e-3) / 2.5e15, 4)}),
         "roofline": {"bound": "hbm", "kernel": "pa_decode_append (main + "
                      "merge pass) inside the loop",
                      "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,

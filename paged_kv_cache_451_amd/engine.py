@@ -168,6 +168,9 @@ class Engine:
         # (start event, end event, KV bytes) of each decode, when timed
         self.time_decode = False
         self.decode_events: List[tuple] = []
+        # (start event, end event, algorithmic flops) of each prefill
+        # attention launch, when timed (with time_decode)
+        self.prefill_events: List[tuple] = []
         if device is not None:
             import torch
             self.torch = torch
@@ -399,8 +402,21 @@ class Engine:
         dev = self.device
         out = torch.empty(n, self.hq, self.d, dtype=torch.bfloat16,
                           device=dev)
+        if self.time_decode:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
         _lib.pa_prefill(q.to(dev), self.k_pool, self.v_pool, *dev_ints,
                         self.scale, out)
+        if self.time_decode:
+            e1.record()
+            # 4 D flops per (query token, attended key) pair and query head;
+            # token i of a chunk attends keys 0..i
+            lo = lens - np.diff(q_start)
+            pairs = int(((lens.astype(np.int64) * (lens + 1) -
+                          lo.astype(np.int64) * (lo + 1)) // 2).sum())
+            self.prefill_events.append(
+                (e0, e1, 4 * self.d * self.hq * pairs))
         if self.mirror:
             self.last_prefill = (q, q_start, tables, lens, out)
 
